@@ -1,0 +1,199 @@
+/*
+ * bdlm_attn.h -- C ABI of the BDLM masked-attention library for AMD MI355X (gfx950).
+ *
+ * The operation (from "Block Parallelism For Efficient Distributed Long-Context
+ * Diffusion Language Model Training", arXiv 2609.19242; abstract and the
+ * evolve.pub review's Summary, Strengths and FAQ):
+ *
+ *   A block diffusion LM trains on the concatenation [x0 ; xt] of L clean and L
+ *   corrupted tokens split into blocks of B tokens.  Across blocks the model is
+ *   autoregressive; inside a block the corrupted tokens are denoised in parallel.
+ *   Clean K/V are shared by every later block, corrupted K/V belong to their own
+ *   block.  Per (batch, q-head h, kv-head g = h / (Hq/Hkv)):
+ *     - a clean query of block b sees the clean keys of blocks <= b;
+ *     - a corrupted query of block b sees the clean keys of blocks < b and the
+ *       corrupted keys of block b;
+ *     - S = scale * <q, k>, LSE = log sum_{visible} exp(S) (natural log),
+ *       P = exp(S - LSE) on visible pairs, O = P V.
+ *   Backward (LSE gets no gradient): D = rowsum(dO * O), dP = dO V^T,
+ *   dS = P (dP - D), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO, dK/dV of a
+ *   kv head summed over the q heads that read it.
+ *
+ *   Because the objective separates over target blocks (block parallelism, BP)
+ *   a rank can compute whole corrupted blocks against the clean prefix, and the
+ *   clean sequence can be sharded (context-sharded BP, CSBP): a block's output
+ *   is then assembled from partials over disjoint clean-key chunks, merged by
+ *   their log-sum-exp; the result equals the length-2L computation up to
+ *   floating-point reduction order (review: Strengths, Prop. 1 / App. A).
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned,
+ *     dense row-major.  Q/K/V/O/dO/dQ/dK/dV use [batch, tokens, heads, head_dim];
+ *     LSE uses [batch, Hq, tokens] fp32.
+ *   - Element type is desc->dtype (BDLM_F32 or BDLM_BF16) unless stated fp32.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  Every argument is
+ *     validated before anything is enqueued; on error the call returns a non-zero
+ *     bdlm_status, enqueues nothing and leaves all outputs untouched.
+ *   - No call allocates device memory.  Scratch memory is the caller's `ws`
+ *     buffer of at least bdlm_attn_workspace_bytes() bytes, which must stay
+ *     alive, and not be shared with a concurrent call, until the stream reaches
+ *     the end of the call.
+ *   - Device faults surface at the caller's next synchronisation.  Calls on
+ *     distinct streams with distinct workspaces are thread-safe.
+ *   - Constraints: L % B == 0, B % 16 == 0, Hq % Hkv == 0, head_dim in {64, 128},
+ *     batch, L, heads >= 1.
+ */
+#ifndef BDLM_ATTN_H
+#define BDLM_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BDLM_OK = 0,
+  BDLM_ERR_INVALID_ARG = 1, /* a shape, pointer, window or id list is invalid */
+  BDLM_ERR_UNSUPPORTED = 2, /* valid but not built (head_dim, too many blocks/parts) */
+  BDLM_ERR_WORKSPACE = 3,   /* ws is NULL or smaller than bdlm_attn_workspace_bytes() */
+  BDLM_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} bdlm_status;
+
+typedef enum { BDLM_F32 = 0, BDLM_BF16 = 1 } bdlm_dtype;
+
+#define BDLM_MAX_LOCAL_BLOCKS 256
+#define BDLM_MAX_MERGE_PARTS 64
+
+/* Problem descriptor (plain data, read during the call only). */
+typedef struct {
+  int32_t batch;          /* >= 1                                                 */
+  int32_t seqlen;         /* L: clean tokens; in full mode also corrupted tokens  */
+  int32_t block;          /* B                                                    */
+  int32_t num_q_heads;    /* Hq                                                   */
+  int32_t num_kv_heads;   /* Hkv, divides Hq (GQA: q head h reads kv head h/(Hq/Hkv)) */
+  int32_t head_dim;       /* 64 or 128                                            */
+  int32_t dtype;          /* bdlm_dtype of Q/K/V/O/dO/dQ/dK/dV                     */
+  float softmax_scale;    /* s in S = s <q, k>; must be finite and > 0            */
+  /* CSBP share mode when num_local_blocks > 0: the queries are whole corrupted
+     blocks of one rank, attending to one clean-key window and (optionally) to
+     their own corrupted block. */
+  int32_t num_local_blocks;   /* 0 = full mode; else 1..BDLM_MAX_LOCAL_BLOCKS      */
+  const int32_t* block_ids;   /* HOST array [num_local_blocks]: global block index of
+                                 each local block, strictly increasing, < L/B       */
+  int32_t kv_begin, kv_end;   /* clean-key window [kv_begin, kv_end) of this call,
+                                 0 <= kv_begin <= kv_end <= L                       */
+  int32_t own_block;          /* 1 = also attend each block's own corrupted K/V     */
+} bdlm_attn_desc;
+
+/* Bytes of scratch memory a call needs (0 is possible).  for_bwd selects
+   bdlm_attn_bwd (1) or bdlm_attn_fwd (0).  Returns 0 for an invalid desc. */
+size_t bdlm_attn_workspace_bytes(const bdlm_attn_desc* desc, int for_bwd);
+
+/* Validate `desc` only (no device work).  Returns a bdlm_status. */
+int bdlm_attn_check_desc(const bdlm_attn_desc* desc);
+
+/*
+ * Forward.
+ * Full mode (num_local_blocks == 0):
+ *   qc, qx [batch, L, Hq, d]; kc, vc, kx, vx [batch, L, Hkv, d] (c = clean x0,
+ *   x = corrupted xt).  Writes oc, ox [batch, L, Hq, d] (dtype) and
+ *   lse_c, lse_x [batch, Hq, L] fp32.
+ * Share mode (num_local_blocks = n > 0):
+ *   qc, oc, lse_c must be NULL.  qx [batch, n*B, Hq, d] and kx, vx
+ *   [batch, n*B, Hkv, d] hold the local corrupted blocks in block_ids order;
+ *   kc, vc [batch, L, Hkv, d] are the whole clean sequence, of which only rows
+ *   [kv_begin, kv_end) are read.  Local block i sees clean keys
+ *   [kv_begin, min(kv_end, block_ids[i]*B)) and, if own_block, its own rows
+ *   [i*B, (i+1)*B) of kx/vx.  Writes the PARTIAL result over exactly those keys
+ *   to ox (fp32, [batch, n*B, Hq, d]) and lse_x (fp32, [batch, Hq, n*B]); rows
+ *   that see no key get O = 0 and LSE = -inf.
+ */
+int bdlm_attn_fwd(const bdlm_attn_desc* desc,
+                  const void* qc, const void* kc, const void* vc,
+                  const void* qx, const void* kx, const void* vx,
+                  void* oc, void* ox, float* lse_c, float* lse_x,
+                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward with the stored-LSE recompute (P is rebuilt from Q, K and LSE).
+ * Full mode: inputs as the forward plus its outputs oc, ox, lse_c, lse_x and the
+ *   upstream gradients doc, dox [batch, L, Hq, d].  Overwrites dqc, dqx
+ *   [batch, L, Hq, d] and dkc, dvc, dkx, dvx [batch, L, Hkv, d] (all dtype).
+ * Share mode: qc, oc, lse_c, doc, dqc must be NULL.  ox is the FINAL (merged)
+ *   output [batch, n*B, Hq, d] in dtype and lse_x the final LSE.  For the keys of
+ *   this call's window:
+ *     - ADDS the dQ contribution into dqx, which is fp32 [batch, n*B, Hq, d]
+ *       (the caller zeroes it once before the first chunk);
+ *     - overwrites rows [kv_begin, kv_end) of dkc, dvc ([batch, L, Hkv, d], dtype;
+ *       rows no local block sees get 0; other rows are untouched);
+ *     - if own_block, overwrites dkx, dvx [batch, n*B, Hkv, d] (dtype); else
+ *       dkx, dvx may be NULL and are not touched.
+ */
+int bdlm_attn_bwd(const bdlm_attn_desc* desc,
+                  const void* qc, const void* kc, const void* vc,
+                  const void* qx, const void* kx, const void* vx,
+                  const void* oc, const void* ox, const float* lse_c, const float* lse_x,
+                  const void* doc, const void* dox,
+                  void* dqc, void* dkc, void* dvc, void* dqx, void* dkx, void* dvx,
+                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Merge attention partials over disjoint key sets (the online (O, LSE) merge of
+ * CSBP's streamed clean prefix):
+ *   LSE = log sum_j exp(LSE_j),  O = sum_j exp(LSE_j - LSE) O_j.
+ * o_parts, lse_parts: HOST arrays of num_parts (1..BDLM_MAX_MERGE_PARTS) DEVICE
+ * pointers; O_j fp32 [batch, tokens, heads, head_dim], LSE_j fp32
+ * [batch, heads, tokens].  Writes o_out in out_dtype and lse_out (fp32).  A
+ * partial with LSE = -inf has weight 0; a row whose partials are all -inf gets
+ * O = 0, LSE = -inf.  o_out / lse_out may alias o_parts[0] / lse_parts[0] (fp32
+ * out_dtype) for an in-place running merge; no other aliasing is allowed.
+ */
+int bdlm_attn_merge_partials(int32_t num_parts, int32_t batch, int64_t tokens,
+                             int32_t heads, int32_t head_dim,
+                             const float* const* o_parts, const float* const* lse_parts,
+                             void* o_out, int32_t out_dtype, float* lse_out,
+                             hipStream_t stream);
+
+/*
+ * Diagnostics: walk the forward (for_bwd = 0) or backward (for_bwd = 1) work
+ * decomposition on the host exactly as the kernels traverse it, for batch 0 and
+ * q-head 0, adding 1 to cover[row * keys + key] (saturating at 255) for every
+ * (query row, key) pair the kernels treat as visible.  Rows are the query rows
+ * of stream 0 followed by stream 1 (full mode: 2L rows; share mode: 0 + n*B);
+ * keys are key array 0 followed by array 1 (full: 2L; share: L + n*B).  cover
+ * may be NULL; otherwise cover_len must hold rows * keys bytes.  stats (may be
+ * NULL) receives 5 values: {workgroups launched, tile visits, tile visits
+ * needing the element mask, pairs marked, consistency errors}.  No device work.
+ */
+int bdlm_attn_schedule_walk(const bdlm_attn_desc* desc, int for_bwd, uint8_t* cover,
+                            int64_t cover_len, int64_t* stats);
+
+/* Human-readable name of a bdlm_status value (static string). */
+const char* bdlm_status_str(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int bdlm_attn_version(void);
+
+/*
+ * Kernel timing (diagnostics).  While enabled, every kernel the library
+ * launches is bracketed by HIP events on its stream.  bdlm_attn_profile_begin
+ * creates a pool of `max_launches` event pairs (the only calls that create HIP
+ * objects); bdlm_attn_profile_end synchronises those events, writes up to
+ * `max_entries` per-kernel totals and destroys the pool.  Not thread-safe.
+ */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} bdlm_kernel_time;
+
+int bdlm_attn_profile_begin(int32_t max_launches);
+int bdlm_attn_profile_end(bdlm_kernel_time* out, int32_t max_entries, int32_t* num_entries);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BDLM_ATTN_H */

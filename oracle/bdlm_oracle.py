@@ -334,10 +334,12 @@ def unit_rows_fwd_bwd(q_rows, k_all, v_all, mask_rows, do_rows, scale):
     return o, lse, dq, dk, dv
 
 
-def sampled_fwd_bwd(qc, kc, vc, qx, kx, vx, doc, dox, block, scale, units):
+def sampled_fwd_bwd(qc, kc, vc, qx, kx, vx, doc, dox, block, scale, units, row_offsets=None):
     """Oracle values on sampled units (batch, stream, block, q-head).
 
-    Returns a list of per-unit dicts (o, lse, dq for the unit's B rows) and the
+    `row_offsets` (optional, offsets inside the block) restricts every unit to
+    those rows; rows are independent, so their values are still exact.
+    Returns a list of per-unit dicts (o, lse, dq for the unit's rows) and the
     summed dK/dV contributions of all sampled rows, [batch, 2L, Hkv, d] -- what
     a backward whose dO is zero outside the sampled rows produces."""
     bsz, L, hq, d = qc.shape
@@ -353,8 +355,9 @@ def sampled_fwd_bwd(qc, kc, vc, qx, kx, vx, doc, dox, block, scale, units):
             kv_cache[(b, g)] = (np.concatenate([kc[b, :, g], kx[b, :, g]]).astype(np.float64),
                                 np.concatenate([vc[b, :, g], vx[b, :, g]]).astype(np.float64))
         k_all, v_all = kv_cache[(b, g)]
-        tok = slice(blk * block, (blk + 1) * block)
-        rows = st * L + np.arange(blk * block, (blk + 1) * block)
+        offs = np.arange(block) if row_offsets is None else np.asarray(row_offsets)
+        tok = blk * block + offs
+        rows = st * L + tok
         q_src = qc if st == 0 else qx
         do_src = doc if st == 0 else dox
         do_rows = None if do_src is None else np.asarray(do_src[b, tok, h], dtype=np.float64)

@@ -1,0 +1,151 @@
+"""GPU parity at sizes the full oracle finishes in seconds: several tiles, ragged
+tails, fp32 and bf16, GQA and MHA, sharp and pre-scaled logits, the CSBP
+share mode with chunked partials, and the merge kernel's edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import masked_attention_bdlm_amd as M
+from oracle import bdlm_oracle as O
+from synth import WORKLOADS, Workload, make_full_inputs, make_share_inputs, to_f64
+from tests.gpu_util import announce, check_outputs, gpu_full, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_full(xh, block, scale):
+    return O.bdlm_fwd_bwd(xh["qc"], xh["kc"], xh["vc"], xh["qx"], xh["kx"], xh["vx"],
+                          xh["doc"], xh["dox"], block, scale)
+
+
+def _case(name, L, B, hq, hkv, d, dtype, batch=1, sharp=False, seed=7):
+    w = Workload(name=name, batch=batch, seqlen=L, block=B, hq=hq, hkv=hkv, head_dim=d,
+                 dtype=dtype, seed=seed, q_std=(1 / 8 if dtype == "f32" else d ** -0.5))
+    return w, sharp
+
+
+def test_tiny_f32_full_oracle():
+    """fp32, batch 1, L=256 + 256, B=16, 2 heads, d=64: full oracle, max abs <= 1e-5."""
+    require_gpu()
+    w = WORKLOADS["tiny_f32"]
+    announce(f"{w.name} L={w.seqlen} B={w.block}")
+    x = make_full_inputs(w, device="cuda")
+    got = host(gpu_full(x, w.block, w.scale))
+    ref = _oracle_full(host(x), w.block, w.scale)
+    check_outputs(got, ref, "f32", where=w.name)
+
+
+SMALL = [
+    _case("f32_ragged_d128", 320, 32, 4, 2, 128, "f32"),
+    _case("f32_b64_d64", 192, 64, 2, 1, 64, "f32", sharp=True),
+    _case("f32_b48_ragged", 144, 48, 2, 2, 128, "f32", batch=2),
+    _case("bf16_ragged_gqa", 320, 32, 4, 2, 128, "bf16"),
+    _case("bf16_ragged_gqa_sharp", 320, 32, 4, 2, 128, "bf16", sharp=True),
+    _case("bf16_mha_d64", 256, 16, 4, 4, 64, "bf16", batch=2),
+    _case("bf16_b128", 512, 128, 4, 1, 128, "bf16", sharp=True),
+    _case("bf16_b48", 144, 48, 2, 2, 128, "bf16"),
+    _case("bf16_one_block", 128, 128, 2, 1, 128, "bf16", sharp=True),
+    _case("bf16_many_tiles", 1024, 64, 8, 2, 128, "bf16", sharp=True),
+]
+
+
+@pytest.mark.parametrize("w,sharp", SMALL, ids=[c[0].name for c in SMALL])
+def test_small_full_oracle(w, sharp):
+    require_gpu()
+    announce(f"{w.name} L={w.seqlen} B={w.block} hq={w.hq} hkv={w.hkv} d={w.head_dim} sharp={sharp}")
+    x = make_full_inputs(w, device="cuda", sharp=sharp)
+    got = host(gpu_full(x, w.block, w.scale))
+    ref = _oracle_full(host(x), w.block, w.scale)
+    check_outputs(got, ref, w.dtype, where=w.name)
+
+
+def _share_flow(x, ids, L, B, chunk, scale, out_dtype):
+    """One rank's CSBP share on the GPU: chunked clean partials and the own-block
+    partial merged online, then the chunked backward with the final O/LSE."""
+    qx, kx, vx, kc, vc, dox = x["qx"], x["kx"], x["vx"], x["kc"], x["vc"], x["dox"]
+    acc = M.share_fwd(qx, kx, vx, kc, vc, ids, B, 0, 0, 1, scale)            # own block
+    for j in range(0, L, chunk):
+        part = M.share_fwd(qx, kx, vx, kc, vc, ids, B, j, min(j + chunk, L), 0, scale)
+        M.merge_partials([acc[0], part[0]], [acc[1], part[1]], torch.float32, out=acc)   # in place
+    o_fin, lse_fin = M.merge_partials([acc[0]], [acc[1]], out_dtype)
+    dqx = torch.zeros(qx.shape, dtype=torch.float32, device=qx.device)
+    dkc, dvc = torch.zeros_like(kc), torch.zeros_like(vc)
+    dkx, dvx = torch.empty_like(kx), torch.empty_like(vx)
+    for j in range(0, L, chunk):
+        M.share_bwd(qx, kx, vx, kc, vc, ids, B, j, min(j + chunk, L), 0, o_fin, lse_fin, dox,
+                    dqx, dkc, dvc, None, None, scale)
+    M.share_bwd(qx, kx, vx, kc, vc, ids, B, 0, 0, 1, o_fin, lse_fin, dox, dqx, dkc, dvc, dkx, dvx, scale)
+    torch.cuda.synchronize()
+    return dict(ox=o_fin, lse_x=lse_fin, dqx=dqx, dkc=dkc, dvc=dvc, dkx=dkx, dvx=dvx)
+
+
+@pytest.mark.parametrize("dtype,L,B,n,chunk,sharp", [
+    ("bf16", 2048, 128, 4, 512, False),
+    ("bf16", 2048, 128, 4, 384, True),      # chunks not aligned to blocks
+    ("bf16", 1024, 64, 5, 256, True),
+    ("f32", 1024, 64, 3, 320, False),
+])
+def test_share_mode_chunked_merge_and_backward(dtype, L, B, n, chunk, sharp):
+    require_gpu()
+    w = Workload(name="share_small", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=128,
+                 dtype=dtype, seed=11, q_std=128 ** -0.5, share_blocks=n, share_chunk=chunk)
+    announce(f"share {dtype} L={L} B={B} n={n} chunk={chunk} sharp={sharp}")
+    x = make_share_inputs(w, device="cuda", sharp=sharp)
+    ids = [int(i) for i in x["block_ids"]]
+    out_dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    got = host(_share_flow(x, ids, L, B, chunk, w.scale, out_dt))
+    xh = host(x)
+    o_ref, lse_ref = O.share_fwd(xh["qx"], xh["kx"], xh["vx"], xh["kc"], xh["vc"], ids, B, 0, L, 1, w.scale)
+    dq, dkc, dvc, dkx, dvx = O.share_bwd(xh["qx"], xh["kx"], xh["vx"], xh["kc"], xh["vc"], ids, B, 0, L, 1,
+                                         o_ref, lse_ref, xh["dox"], w.scale)
+    ref = dict(ox=o_ref, lse_x=lse_ref, dqx=dq, dkc=dkc, dvc=dvc, dkx=dkx, dvx=dvx)
+    check_outputs(got, ref, dtype, where="share")
+
+
+def test_share_partial_of_empty_window_is_minus_inf():
+    require_gpu()
+    w = Workload(name="share_empty", batch=1, seqlen=1024, block=64, hq=2, hkv=1, head_dim=64,
+                 dtype="bf16", seed=12, q_std=0.125, share_blocks=3)
+    x = make_share_inputs(w, device="cuda")
+    ids = [int(i) for i in x["block_ids"]]
+    lo = max(ids) * 64            # window above every block's clean prefix
+    o, lse = M.share_fwd(x["qx"], x["kx"], x["vx"], x["kc"], x["vc"], ids, 64, lo, 1024, 0)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_merge_kernel_edge_cases():
+    require_gpu()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    b, T, H, d = 2, 77, 3, 128
+    o = [torch.randn((b, T, H, d), generator=g, device="cuda") for _ in range(3)]
+    lse = [torch.randn((b, H, T), generator=g, device="cuda") for _ in range(3)]
+    # some rows empty in some parts, some rows empty everywhere
+    for j in range(3):
+        lse[j][:, :, j::5] = -float("inf")
+        o[j][:, j::5] = 0
+    lse_all_empty = [x.clone() for x in lse]
+    for x in lse_all_empty:
+        x[:, :, 70:] = -float("inf")
+    oh = [to_f64(x) for x in o]
+    for parts_lse in (lse, lse_all_empty):
+        lh = [to_f64(x) for x in parts_lse]
+        ref_o, ref_l = O.merge_partials(oh, lh)
+        for out_dt in (torch.float32, torch.bfloat16):
+            mo, ml = M.merge_partials(o, parts_lse, out_dt)
+            torch.cuda.synchronize()
+            mo_h, ml_h = to_f64(mo), to_f64(ml)
+            tol = 1e-5 if out_dt == torch.float32 else 2e-2
+            assert np.max(np.abs(mo_h - ref_o)) <= tol
+            fin = np.isfinite(ref_l)
+            assert (np.isneginf(ml_h) == ~fin).all()
+            assert np.max(np.abs(ml_h[fin] - ref_l[fin])) <= 1e-5
+    # in place (fp32 output aliasing part 0) and a single part
+    acc_o, acc_l = o[0].clone(), lse[0].clone()
+    M.merge_partials([acc_o, o[1]], [acc_l, lse[1]], torch.float32, out=(acc_o, acc_l))
+    ref_o, ref_l = O.merge_partials(oh[:2], [to_f64(lse[0]), to_f64(lse[1])])
+    torch.cuda.synchronize()
+    assert np.max(np.abs(to_f64(acc_o) - ref_o)) <= 1e-5
+    so, sl = M.merge_partials([o[2]], [lse[2]], torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(so, o[2]) or np.max(np.abs(to_f64(so) - oh[2])) <= 1e-6

@@ -1,0 +1,183 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched):
+exported symbols, argument validation, workspace sizing, and the kernels'
+work decomposition walked on the host against the oracle's explicit mask."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import masked_attention_bdlm_amd as M
+from masked_attention_bdlm_amd import _lib
+from masked_attention_bdlm_amd._lib import make_desc
+from oracle import bdlm_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bdlm_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bdlm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = M.load()
+    declared = _declared_functions()
+    assert len(declared) >= 8
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (bdlm_\w+)", out))
+    assert set(declared) <= exported
+    assert set(_lib.EXPORTED) == set(declared)
+    assert lib.bdlm_attn_version() >= 100
+
+
+def _ok_desc(**kw):
+    base = dict(batch=1, seqlen=256, block=16, hq=4, hkv=2, head_dim=64, dtype=1, scale=0.125)
+    base.update(kw)
+    return make_desc(base["batch"], base["seqlen"], base["block"], base["hq"], base["hkv"],
+                     base["head_dim"], base["dtype"], base["scale"], base.get("block_ids"),
+                     base.get("kv_begin", 0), base.get("kv_end", 0), base.get("own_block", 0))
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    ({"seqlen": 250}, 1),            # L % B != 0
+    ({"block": 8, "seqlen": 256}, 1),  # B % 16 != 0
+    ({"block": 24, "seqlen": 240}, 1),
+    ({"hq": 3, "hkv": 2}, 1),        # Hq % Hkv != 0
+    ({"head_dim": 96}, 2),
+    ({"head_dim": 256}, 2),
+    ({"dtype": 7}, 1),
+    ({"scale": 0.0}, 1),
+    ({"scale": float("nan")}, 1),
+    ({"batch": 0}, 1),
+    ({"block_ids": [3, 2], "kv_begin": 0, "kv_end": 64}, 1),      # not increasing
+    ({"block_ids": [1, 16], "kv_begin": 0, "kv_end": 64}, 1),     # id >= L/B
+    ({"block_ids": [1, 5], "kv_begin": 32, "kv_end": 16}, 1),     # bad window
+    ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 300}, 1),
+    ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "own_block": 2}, 1),
+    ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "own_block": 1}, 0),
+    ({"seqlen": 8192, "block": 16, "block_ids": list(range(300)), "kv_begin": 0, "kv_end": 16}, 2),
+])
+def test_descriptor_validation(kw, code):
+    d = _ok_desc(**kw)
+    assert M.load().bdlm_attn_check_desc(ctypes.byref(d)) == code
+
+
+def test_calls_reject_bad_arguments_before_launch():
+    lib = M.load()
+    d = _ok_desc()
+    p = ctypes.c_void_p(4096)          # never dereferenced: validation fails first
+    mis = ctypes.c_void_p(4096 + 8)
+    n = None
+    # missing outputs
+    assert lib.bdlm_attn_fwd(ctypes.byref(d), p, p, p, p, p, p, p, n, p, p, n, 0, n) == 1
+    # misaligned input
+    assert lib.bdlm_attn_fwd(ctypes.byref(d), mis, p, p, p, p, p, p, p, p, p, n, 0, n) == 1
+    # invalid descriptor wins over pointers
+    bad = _ok_desc(seqlen=250)
+    assert lib.bdlm_attn_fwd(ctypes.byref(bad), p, p, p, p, p, p, p, p, p, p, n, 0, n) == 1
+    # share mode must not get clean queries
+    sd = _ok_desc(block_ids=[2, 5], kv_begin=0, kv_end=64, own_block=1)
+    assert lib.bdlm_attn_fwd(ctypes.byref(sd), p, p, p, p, p, p, n, p, n, p, n, 0, n) == 1
+    # backward: workspace missing / too small
+    args = [p] * 18
+    assert lib.bdlm_attn_bwd(ctypes.byref(d), *args, n, 0, n) == 3
+    need = lib.bdlm_attn_workspace_bytes(ctypes.byref(d), 1)
+    assert need > 0
+    assert lib.bdlm_attn_bwd(ctypes.byref(d), *args, p, need - 1, n) == 3
+    # merge: too many parts / bad head_dim / aliasing a later part / bf16 in place
+    arr = (ctypes.c_void_p * 2)(4096, 8192)
+    assert lib.bdlm_attn_merge_partials(65, 1, 16, 2, 64, arr, arr, p, 0, p, n) == 2
+    assert lib.bdlm_attn_merge_partials(2, 1, 16, 2, 48, arr, arr, p, 0, p, n) == 2
+    assert lib.bdlm_attn_merge_partials(2, 1, 16, 2, 64, arr, arr, ctypes.c_void_p(8192), 0,
+                                        ctypes.c_void_p(1 << 20), n) == 1
+    assert lib.bdlm_attn_merge_partials(2, 1, 16, 2, 64, arr, arr, ctypes.c_void_p(4096), 1,
+                                        ctypes.c_void_p(1 << 20), n) == 1
+    assert _lib.status_str(3).startswith("workspace")
+
+
+def test_workspace_sizes():
+    lib = M.load()
+    d = _ok_desc(batch=2, seqlen=512, hq=4, hkv=2, head_dim=128)
+    assert lib.bdlm_attn_workspace_bytes(ctypes.byref(d), 0) == 0
+    ws = lib.bdlm_attn_workspace_bytes(ctypes.byref(d), 1)
+    # D per stream + fp32 dQ per stream
+    assert ws >= 2 * 4 * 2 * 4 * 512 + 2 * 4 * 2 * 512 * 4 * 128
+    sd = _ok_desc(block_ids=[1, 3], kv_begin=0, kv_end=64)
+    assert lib.bdlm_attn_workspace_bytes(ctypes.byref(sd), 1) >= 4 * 4 * 32
+    assert lib.bdlm_attn_workspace_bytes(ctypes.byref(_ok_desc(seqlen=250)), 1) == 0
+
+
+# ------------------------------------------------ schedule coverage == oracle mask
+FULL_CASES = [
+    (256, 16, 2, 2, 64, 0),     # tiny fp32 shape
+    (256, 16, 2, 2, 64, 1),
+    (320, 32, 4, 2, 128, 1),    # ragged tiles (L not a multiple of 128)
+    (192, 64, 2, 1, 128, 1),
+    (512, 128, 2, 1, 128, 1),
+    (1024, 256, 2, 2, 64, 1),
+    (128, 128, 1, 1, 64, 1),    # B = L: one block
+    (144, 48, 2, 2, 128, 0),    # B not a power of two
+    (96, 16, 3, 1, 64, 1),
+]
+
+
+@pytest.mark.parametrize("L,B,hq,hkv,d,dt", FULL_CASES)
+@pytest.mark.parametrize("for_bwd", [0, 1])
+def test_full_schedule_covers_exactly_the_mask(L, B, hq, hkv, d, dt, for_bwd):
+    desc = make_desc(1, L, B, hq, hkv, d, dt, 0.1)
+    cover, st = M.schedule_walk(desc, for_bwd)
+    assert st["errors"] == 0
+    np.testing.assert_array_equal(cover, O.bdlm_mask(L, B).astype(np.uint8))
+    assert st["pairs"] == L * (L + B)
+
+
+@pytest.mark.parametrize("batch,hkv", [(1, 8), (2, 8), (3, 4), (2, 16)])
+def test_workgroup_decode_is_a_bijection(batch, hkv):
+    desc = make_desc(batch, 512, 64, 4 * hkv, hkv, 128, 1, 0.1)
+    for for_bwd in (0, 1):
+        _, st = M.schedule_walk(desc, for_bwd, want_cover=False)
+        assert st["errors"] == 0
+
+
+SHARE_CASES = [
+    # L, B, ids, window, own
+    (512, 16, [0, 3, 7, 20, 31], (0, 512), 1),
+    (512, 16, [0, 3, 7, 20, 31], (128, 256), 0),
+    (512, 16, [0, 3, 7, 20, 31], (0, 0), 1),
+    (1024, 128, [1, 4, 7], (256, 512), 0),
+    (1024, 128, [1, 4, 7], (0, 1024), 1),
+    (1024, 64, [2, 9, 10, 15], (100, 700), 1),     # unaligned window
+    (4096, 1024, [0, 3], (0, 4096), 1),
+]
+
+
+@pytest.mark.parametrize("L,B,ids,win,own", SHARE_CASES)
+@pytest.mark.parametrize("for_bwd", [0, 1])
+def test_share_schedule_covers_exactly_the_key_sets(L, B, ids, win, own, for_bwd):
+    desc = make_desc(1, L, B, 2, 1, 128, 1, 0.1, ids, win[0], win[1], own)
+    cover, st = M.schedule_walk(desc, for_bwd)
+    assert st["errors"] == 0
+    n = len(ids)
+    expect = np.zeros((n * B, L + n * B), dtype=np.uint8)
+    for i, bid in enumerate(ids):
+        clean, mine = O.share_keys(bid, B, i, win[0], win[1], own)
+        expect[i * B:(i + 1) * B, clean] = 1
+        expect[i * B:(i + 1) * B, L + mine] = 1
+    np.testing.assert_array_equal(cover, expect)
+
+
+def test_masked_tiles_are_few_when_tiles_divide_blocks():
+    # B a multiple of every tile size: only edge tiles of the range need masks
+    desc = make_desc(1, 4096, 256, 1, 1, 128, 1, 0.1)
+    _, st = M.schedule_walk(desc, 0, want_cover=False)
+    assert st["masked_visits"] == 0
+    _, stb = M.schedule_walk(desc, 1, want_cover=False)
+    assert stb["masked_visits"] == 0
