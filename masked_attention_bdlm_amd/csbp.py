@@ -1,0 +1,96 @@
+"""One rank's context-sharded block-parallel (CSBP) attention share, on one GPU.
+
+Block parallelism gives a rank whole corrupted blocks; CSBP additionally shards
+the shared clean sequence, so the rank sees the clean K/V prefix as a stream of
+chunks ("Block Parallelism For Efficient Distributed Long-Context Diffusion
+Language Model Training": abstract; review FAQ "What is CSBP?").  This module
+drives that stream with the C-ABI calls:
+
+forward   own-block partial, then per clean chunk a share-mode partial merged
+          into the running (O, LSE) in place; the last merge writes O in the
+          input dtype.
+backward  per clean chunk a share-mode backward with the final O and LSE (dQ
+          added into one fp32 buffer, the chunk's clean dK/dV written at its
+          window), plus the own-block backward.
+
+Chunks that no local block can see (start >= max(block_ids) * B) are skipped.
+Inside a chunk, blocks whose clean prefix ends before the chunk get the empty
+partial (O = 0, LSE = -inf), which the merge kernel recognises without reading
+its O.
+"""
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+from .api import bdlm_attn_bwd, bdlm_attn_fwd, bdlm_attn_merge_partials, desc_for, workspace
+
+
+class ShareBuffers:
+    """Preallocated buffers of a share step (so the timed loop allocates nothing)."""
+
+    def __init__(self, qx: torch.Tensor, kc: torch.Tensor, kx: torch.Tensor):
+        b, T, hq, d = qx.shape
+        dev = qx.device
+        self.acc_o = torch.empty((b, T, hq, d), dtype=torch.float32, device=dev)
+        self.acc_lse = torch.empty((b, hq, T), dtype=torch.float32, device=dev)
+        self.part_o = torch.empty_like(self.acc_o)
+        self.part_lse = torch.empty_like(self.acc_lse)
+        self.o = torch.empty_like(qx)
+        self.lse = torch.empty_like(self.acc_lse)
+        self.dqx = torch.empty((b, T, hq, d), dtype=torch.float32, device=dev)
+        self.dkc = torch.zeros_like(kc)
+        self.dvc = torch.zeros_like(kc)
+        self.dkx = torch.empty_like(kx)
+        self.dvx = torch.empty_like(kx)
+        self.ws = None
+
+
+def _chunks(L: int, chunk: int, ids: Sequence[int], B: int) -> List[Tuple[int, int]]:
+    """Chunks [start, end) of the clean sequence that at least one local block sees."""
+    top = max(ids) * B
+    return [(j, min(j + chunk, L)) for j in range(0, min(L, top), chunk)]
+
+
+def share_forward(qx, kx, vx, kc, vc, ids: Sequence[int], B: int, chunk: int,
+                  scale: Optional[float] = None, bufs: Optional[ShareBuffers] = None, stream=None):
+    """Final (O, LSE) of the local corrupted blocks over their whole visible key
+    set, assembled from streamed chunk partials.  Returns (O in qx.dtype, LSE)."""
+    if qx.shape[0] != 1:
+        raise ValueError("the share step streams one sequence (batch 1)")
+    ids = [int(i) for i in ids]
+    L = kc.shape[1]
+    bufs = bufs or ShareBuffers(qx, kc, kx)
+    d_own = desc_for(qx, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=0, kv_end=0, own_block=1)
+    bdlm_attn_fwd(d_own, None, kc, vc, qx, kx, vx, None, bufs.acc_o, None, bufs.acc_lse, None, stream)
+    for (j0, j1) in _chunks(L, chunk, ids, B):
+        d = desc_for(qx, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=j0, kv_end=j1, own_block=0)
+        bdlm_attn_fwd(d, None, kc, vc, qx, kx, vx, None, bufs.part_o, None, bufs.part_lse, None, stream)
+        bdlm_attn_merge_partials([bufs.acc_o, bufs.part_o], [bufs.acc_lse, bufs.part_lse],
+                                 bufs.acc_o, bufs.acc_lse, stream)
+    bdlm_attn_merge_partials([bufs.acc_o], [bufs.acc_lse], bufs.o, bufs.lse, stream)
+    return bufs.o, bufs.lse
+
+
+def share_backward(qx, kx, vx, kc, vc, ids: Sequence[int], B: int, chunk: int, o, lse, dox,
+                   scale: Optional[float] = None, bufs: Optional[ShareBuffers] = None, stream=None):
+    """Gradients of the share: returns (dqx fp32, dkc, dvc, dkx, dvx).  dkc/dvc
+    rows that no local block sees are zero."""
+    ids = [int(i) for i in ids]
+    L = kc.shape[1]
+    bufs = bufs or ShareBuffers(qx, kc, kx)
+    bufs.dqx.zero_()
+    top = max(ids) * B
+    if top < L:
+        bufs.dkc[:, top:].zero_()
+        bufs.dvc[:, top:].zero_()
+    d_full = desc_for(qx, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=0, kv_end=L, own_block=1)
+    if bufs.ws is None:
+        bufs.ws = workspace(d_full, True, qx.device)
+    for (j0, j1) in _chunks(L, chunk, ids, B):
+        d = desc_for(qx, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=j0, kv_end=j1, own_block=0)
+        bdlm_attn_bwd(d, None, kc, vc, qx, kx, vx, None, o, None, lse, None, dox,
+                      None, bufs.dkc, bufs.dvc, bufs.dqx, None, None, bufs.ws, stream)
+    d_own = desc_for(qx, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=0, kv_end=0, own_block=1)
+    bdlm_attn_bwd(d_own, None, kc, vc, qx, kx, vx, None, o, None, lse, None, dox,
+                  None, bufs.dkc, bufs.dvc, bufs.dqx, bufs.dkx, bufs.dvx, bufs.ws, stream)
+    return bufs.dqx, bufs.dkc, bufs.dvc, bufs.dkx, bufs.dvx

@@ -312,6 +312,7 @@ int bdlm_attn_merge_partials(int32_t num_parts, int32_t batch, int64_t tokens, i
   }
   a.nparts = num_parts; a.batch = batch; a.tokens = tokens; a.heads = heads; a.D = head_dim;
   a.o_out = o_out; a.lse_out = lse_out;
+  a.inplace = (o_parts[0] == o_out && lse_parts[0] == lse_out) ? 1 : 0;
   ProfScope ps("bdlm_merge", stream);
   return launch_merge(a, out_dtype == BDLM_BF16, stream) == hipSuccess ? BDLM_OK : BDLM_ERR_HIP;
 }

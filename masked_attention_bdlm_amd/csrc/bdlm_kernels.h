@@ -50,6 +50,7 @@ struct BwdArgs {
 
 struct MergeArgs {
   int nparts, batch, heads, D;
+  int inplace;          // 1: o_out/lse_out alias part 0
   int64_t tokens;
   const float* o[kMaxMergeParts];
   const float* lse[kMaxMergeParts];

@@ -73,6 +73,33 @@ __device__ inline void stage_rows_t(T* lds, const T* base, int64_t rs, int k0, i
   }
 }
 
+// Copy rows [k0, k0+NR) into LDS twice from one global read: row-major
+// (lds_r[row * ST + d]) and transposed (lds_t[d * STT + row]).
+template <typename T, int NR, int D, int ST, int STT>
+__device__ inline void stage_rows_dual(T* lds_r, T* lds_t, const T* base, int64_t rs, int k0, int kmax,
+                                       int tid) {
+  constexpr int VEC = Elt<T>::VEC;
+  constexpr int RPT = NR * D / (256 * VEC);
+  static_assert(RPT >= 1 && NR * D == 256 * VEC * RPT, "tile/thread mismatch");
+  constexpr int RG = NR / RPT;
+  const int rg = tid % RG, dc = tid / RG;
+  const int col = dc * VEC;
+  Vec16 v[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int k = k0 + rg * RPT + j;
+    v[j] = (k < kmax) ? ld16(base + (int64_t)k * rs + col) : zero16();
+  }
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) st16(lds_r + (rg * RPT + j) * ST + col, v[j]);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    T* dst = lds_t + (col + e) * STT + rg * RPT;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) dst[j] = elem_of<T>(v[j], e);
+  }
+}
+
 // ================================================================= forward
 template <typename T, int D, bool OUT_F32>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs args) {
@@ -285,7 +312,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
   __shared__ __attribute__((aligned(16))) T dot_lds[D * QTST];
   __shared__ __attribute__((aligned(16))) T ds_lds[M * DSST];
   __shared__ __attribute__((aligned(16))) T kt_lds[D * KTST];
-  __shared__ float lse_l[M], dl_l[M];
+  __shared__ __attribute__((aligned(16))) float lse_l[M];
+  __shared__ __attribute__((aligned(16))) float dl_l[M];
   __shared__ int lo_l[M], hi_l[M];
 
   const Problem& p = args.p;
@@ -339,10 +367,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
         const T* qb = reinterpret_cast<const T*>(args.q[s]) + (int64_t)b * R * qrs + (int64_t)h * D;
         const T* db = reinterpret_cast<const T*>(args.dout[s]) + (int64_t)b * R * qrs + (int64_t)h * D;
         __syncthreads();
-        stage_rows<T, M, D, QST>(q_lds, qb, qrs, q0, q1, tid);
-        stage_rows<T, M, D, QST>(do_lds, db, qrs, q0, q1, tid);
-        stage_rows_t<T, M, D, QTST>(qt_lds, qb, qrs, q0, q1, tid);
-        stage_rows_t<T, M, D, QTST>(dot_lds, db, qrs, q0, q1, tid);
+        stage_rows_dual<T, M, D, QST, QTST>(q_lds, qt_lds, qb, qrs, q0, q1, tid);
+        stage_rows_dual<T, M, D, QST, QTST>(do_lds, dot_lds, db, qrs, q0, q1, tid);
         if (tid < M) {
           const int rr = q0 + tid;
           int lo = 0, hi = 0;
@@ -376,13 +402,20 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rr = qs * 32 + c_row(i, hh);
-            bool vis = true;
-            if (need_mask) vis = kk >= lo_l[rr] && kk < hi_l[rr];
-            const float pe = vis ? fast_exp2(sacc[qs][i] * sl2 - lse_l[rr]) : 0.f;
-            pv[qs][i] = pe;
-            dsv[qs][i] = pe * (pacc[qs][i] - dl_l[rr]);
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int rr0 = qs * 32 + c_row(4 * i4, hh);      // 4 consecutive rows
+            const float4 l4 = *reinterpret_cast<const float4*>(lse_l + rr0);
+            const float4 d4 = *reinterpret_cast<const float4*>(dl_l + rr0);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = 4 * i4 + j;
+              float pe = fast_exp2(sacc[qs][i] * sl2 - lv[j]);
+              if (need_mask && !(kk >= lo_l[rr0 + j] && kk < hi_l[rr0 + j])) pe = 0.f;
+              pv[qs][i] = pe;
+              dsv[qs][i] = pe * (pacc[qs][i] - dv[j]);
+            }
           }
         }
         // dV_w += P^T dO ; dK_w += dS^T Q   (k = queries in C-row order)
@@ -408,23 +441,26 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
           }
         }
         __syncthreads();
-        // dQ^T[d][query] = K^T[d][key] dS^T[key][query], added into fp32 dQ
+        // dQ[query][d] = dS[query][key] K[key][d], added into fp32 dQ
         float* dqb = args.dq_acc[s] + (int64_t)b * R * qrs + (int64_t)h * D;
         constexpr int TILES = (D / 32) * QS;
         for (int tt = w; tt < TILES; tt += 4) {
           const int dt = tt % (D / 32), qs = tt / (D / 32);
+          // rows = queries (A = dS from LDS), columns = head_dim (B = K^T from LDS):
+          // each lane owns one d, so an atomic instruction covers 2 x 32
+          // consecutive floats of two dQ rows.
           f32x16 acc = f32x16{};
 #pragma unroll
           for (int c = 0; c < N / KC; ++c) {
-            Frag ka = ld_frag<T>(kt_lds + (dt * 32 + ln) * KTST + c * KC + hh * KPL);
-            Frag sb = ld_frag<T>(ds_lds + (qs * 32 + ln) * DSST + c * KC + hh * KPL);
-            acc = E::mma(ka, sb, acc);
+            Frag sa = ld_frag<T>(ds_lds + (qs * 32 + ln) * DSST + c * KC + hh * KPL);
+            Frag kb2 = ld_frag<T>(kt_lds + (dt * 32 + ln) * KTST + c * KC + hh * KPL);
+            acc = E::mma(sa, kb2, acc);
           }
-          const int rr = q0 + qs * 32 + ln;
-          if (rr < q1) {
-            float* dst = dqb + (int64_t)rr * qrs + dt * 32;
+          float* dst = dqb + dt * 32 + ln;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) unsafeAtomicAdd(dst + c_row(i, hh), acc[i] * args.scale);
+          for (int i = 0; i < 16; ++i) {
+            const int rr = q0 + qs * 32 + c_row(i, hh);
+            if (rr < q1) unsafeAtomicAdd(dst + (int64_t)rr * qrs, acc[i] * args.scale);
           }
         }
       }
@@ -477,12 +513,22 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs args) {
   const int64_t oi = row * D + part * 4;
 
   float m = -INFINITY;
-  for (int j = 0; j < args.nparts; ++j) m = fmaxf(m, args.lse[j][li]);
+  int live = 0;
+  for (int j = 0; j < args.nparts; ++j) {
+    const float l = args.lse[j][li];
+    m = fmaxf(m, l);
+    live += (j > 0 && l != -INFINITY);
+  }
+  // In place (output aliases part 0): a row where every other part is empty
+  // keeps its values, so it is neither read nor written.
+  if (args.inplace && live == 0) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float tot = 0.f;
   if (m != -INFINITY) {
     for (int j = 0; j < args.nparts; ++j) {
-      const float wj = __expf(args.lse[j][li] - m);
+      const float l = args.lse[j][li];
+      if (l == -INFINITY) continue;              // weight 0: O_j is not read
+      const float wj = __expf(l - m);
       const float4 v = *reinterpret_cast<const float4*>(args.o[j] + oi);
       tot += wj;
       acc.x += wj * v.x; acc.y += wj * v.y; acc.z += wj * v.z; acc.w += wj * v.w;

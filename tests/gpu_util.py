@@ -82,3 +82,38 @@ def check_outputs(got, ref, dtype, keys=None, where=""):
             report[k] = e
             assert e <= TOL_REL, f"{where} {k}: rel fro {e:.3e} > {TOL_REL}"
     return report
+
+
+class HostView:
+    """Lazy host fp64 view of a device tensor: indexing copies only the
+    requested slice, so the oracle can read sampled rows of large inputs."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, idx):
+        if not isinstance(idx, tuple):
+            idx = (idx,)
+        idx = tuple(torch.as_tensor(i, device=self.t.device) if isinstance(i, np.ndarray) else i for i in idx)
+        return to_f64(self.t[idx])
+
+
+def row_sample(block: int, count: int, seed: int) -> np.ndarray:
+    """Offsets inside a block: first and last row plus a seeded subset."""
+    if count >= block:
+        return np.arange(block)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, block - 1), size=count - 2, replace=False)
+    return np.sort(np.concatenate([[0, block - 1], mid]))
+
+
+def mask_dout(x, units, offs, block):
+    """Copies of dOc/dOx that keep only the sampled rows (blk*block + offs of
+    head h in each unit (b, stream, blk, h)) and are zero elsewhere."""
+    doc, dox = torch.zeros_like(x["doc"]), torch.zeros_like(x["dox"])
+    for (b, st, blk, h) in np.asarray(units).tolist():
+        rows = torch.as_tensor(blk * block + np.asarray(offs), device=doc.device)
+        src, dst = (x["doc"], doc) if st == 0 else (x["dox"], dox)
+        dst[b, rows, h] = src[b, rows, h]
+    return doc, dox
