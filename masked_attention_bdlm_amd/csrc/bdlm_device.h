@@ -44,14 +44,18 @@ template <> struct Elt<float> {
 };
 
 // 16-byte vector of VEC elements.
-struct alignas(16) Vec16 { uint32_t w[4]; };
+typedef uint32_t Vec16 __attribute__((ext_vector_type(4)));
 
 __device__ inline Vec16 ld16(const void* p) { return *reinterpret_cast<const Vec16*>(p); }
 __device__ inline void st16(void* p, const Vec16& v) { *reinterpret_cast<Vec16*>(p) = v; }
-__device__ inline Vec16 zero16() { Vec16 v; v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0u; return v; }
+__device__ inline Vec16 zero16() { return Vec16{0u, 0u, 0u, 0u}; }
 
-template <typename T> __device__ inline T elem_of(const Vec16& v, int j) {
-  return reinterpret_cast<const T*>(&v)[j];
+template <typename T> __device__ inline T elem_of(const Vec16& v, int j);
+template <> __device__ inline bf16 elem_of<bf16>(const Vec16& v, int j) {
+  return __builtin_bit_cast(bf16x8, v)[j];
+}
+template <> __device__ inline float elem_of<float>(const Vec16& v, int j) {
+  return __builtin_bit_cast(f32x4, v)[j];
 }
 
 // KPL contiguous elements at p (A/B fragment along k).
@@ -79,6 +83,55 @@ template <> __device__ inline float ld_frag_crows<float>(const float* row, int c
   return row[c_row(ci, hh)];
 }
 
+// ---- fragments read "down" a row-major LDS tile (k = tile rows, lane = column)
+//
+// ds_read_b64_tr_b16 (gfx950): in each 16-lane group, lane r supplies the
+// address of 4 consecutive 16-bit elements, forming a 16x4 matrix M[r][c];
+// lane i receives M[4j + i/4][i%4] for j = 0..3.  If lane r addresses
+// tile[r0 + r/4][c0 + 4*(r%4)], lane i receives tile[r0 + j][c0 + i], j=0..3:
+// column c0 + i of rows r0..r0+3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ inline bf16x4 ld_tr4(const bf16* tile, int stride, int r0, int c0, int i16) {
+  const bf16* p = tile + (r0 + (i16 >> 2)) * stride + c0 + 4 * (i16 & 3);
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ inline bf16x8 cat44(bf16x4 lo, bf16x4 hi) {
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// MFMA fragment for column col0 + lane%32 whose k values are the tile rows
+// row0 + c_row(ci*KPL + j, hh), j < KPL (the C-layout row order of chunk ci).
+template <typename T> __device__ inline typename Elt<T>::Frag ld_frag_kcrow(const T* tile, int stride, int row0,
+                                                                         int ci, int lane, int col0);
+template <> __device__ inline bf16x8 ld_frag_kcrow<bf16>(const bf16* tile, int stride, int row0, int ci, int lane,
+                                                        int col0) {
+  const int r = row0 + 16 * ci + 4 * (lane >> 5);
+  const int c = col0 + ((lane >> 4) & 1) * 16;
+  return cat44(ld_tr4(tile, stride, r, c, lane & 15), ld_tr4(tile, stride, r + 8, c, lane & 15));
+}
+template <> __device__ inline float ld_frag_kcrow<float>(const float* tile, int stride, int row0, int ci, int lane,
+                                                        int col0) {
+  return tile[(row0 + c_row(ci, lane >> 5)) * stride + col0 + (lane & 31)];
+}
+
+// Same with the natural k order: rows row0 + KPL*hh + j, j < KPL.
+template <typename T> __device__ inline typename Elt<T>::Frag ld_frag_knat(const T* tile, int stride, int row0,
+                                                                        int lane, int col0);
+template <> __device__ inline bf16x8 ld_frag_knat<bf16>(const bf16* tile, int stride, int row0, int lane, int col0) {
+  const int r = row0 + 8 * (lane >> 5);
+  const int c = col0 + ((lane >> 4) & 1) * 16;
+  return cat44(ld_tr4(tile, stride, r, c, lane & 15), ld_tr4(tile, stride, r + 4, c, lane & 15));
+}
+template <> __device__ inline float ld_frag_knat<float>(const float* tile, int stride, int row0, int lane, int col0) {
+  return tile[(row0 + (lane >> 5)) * stride + col0 + (lane & 31)];
+}
+
 // Pack C-layout values acc[ci*KPL .. ci*KPL+KPL) into an MFMA fragment.
 template <typename T> __device__ inline typename Elt<T>::Frag pack_frag(const float* v);
 template <> __device__ inline bf16x8 pack_frag<bf16>(const float* v) {
@@ -88,6 +141,22 @@ template <> __device__ inline bf16x8 pack_frag<bf16>(const float* v) {
   return r;
 }
 template <> __device__ inline float pack_frag<float>(const float* v) { return v[0]; }
+
+// Store the KPL values of fragment f (C-layout rows c_row(ci*KPL + j, hh) of a
+// 32-row tile) into one row of a k-major LDS buffer (`row` points at the
+// tile's first row): bf16 as two 8-byte runs of 4 consecutive rows.
+template <typename T> __device__ inline void store_crow_run(T* row, int ci, int hh, typename Elt<T>::Frag f);
+template <> __device__ inline void store_crow_run<bf16>(bf16* row, int ci, int hh, bf16x8 f) {
+  bf16* p = row + 16 * ci + 4 * hh;
+  bf16x4 lo, hi;
+  lo[0] = f[0]; lo[1] = f[1]; lo[2] = f[2]; lo[3] = f[3];
+  hi[0] = f[4]; hi[1] = f[5]; hi[2] = f[6]; hi[3] = f[7];
+  *reinterpret_cast<bf16x4*>(p) = lo;
+  *reinterpret_cast<bf16x4*>(p + 8) = hi;
+}
+template <> __device__ inline void store_crow_run<float>(float* row, int ci, int hh, float f) {
+  row[c_row(ci, hh)] = f;
+}
 
 template <typename T> __device__ inline T to_elt(float x) { return static_cast<T>(x); }
 

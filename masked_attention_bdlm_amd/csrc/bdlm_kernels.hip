@@ -6,18 +6,20 @@
 // the online softmax (max, exp2, sum, rescale) is lane-local except one swap
 // between the two lane halves.  P^T then feeds O^T += V^T P^T directly from
 // registers (its k order is the C-layout row order, which the V^T fragment
-// loads reproduce), so P never touches LDS.  K tiles are staged row-major in
-// LDS, V tiles transposed.  Only key tiles inside a row's visible ranges are
-// visited; tiles on a range edge test each element against [lo, hi).
+// loads reproduce), so P never touches LDS.  K and V tiles are staged
+// row-major in LDS; V^T fragments are read with the gfx950 LDS transpose
+// load.  Only key tiles inside a row's visible ranges are visited; tiles on a
+// range edge test each element against [lo, hi).
 //
 // Backward (stored-LSE recompute, "dK/dV accumulated per key tile"): one
 // workgroup per (batch, kv-head, key array, 128-key tile); wave w owns 32 keys
 // and keeps K_w, V_w and its dK_w, dV_w accumulators in registers while it loops
 // over the visible query tiles of every q head of the GQA group.  S and dP are
 // computed with the query as MFMA row, so P and dS (lane = key) are directly the
-// A operands of dV += P^T dO and dK += dS^T Q; dO^T and Q^T come from LDS tiles
-// staged transposed.  dS goes through LDS once more for dQ^T = K^T dS^T, which
-// is added into an fp32 accumulator with hardware float atomics.
+// A operands of dV += P^T dO and dK += dS^T Q, whose dO / Q operands are read
+// transposed out of the row-major (double-buffered) LDS tiles.  dS goes
+// through LDS once more for dQ = dS K, which is added into an fp32 accumulator
+// with hardware float atomics, lanes along head_dim.
 
 #include <hip/hip_runtime.h>
 
@@ -109,10 +111,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs args) {
   constexpr int KPL = E::KPL, KC = 2 * KPL;
   constexpr int DCH = D / KC;          // k-chunks over head_dim
   constexpr int CPS = 32 / KC;         // k-chunks per 32-key subtile
-  constexpr int KST = D + E::PAD;      // K tile row stride
-  constexpr int VST = N + E::PAD;      // V^T tile row stride
+  constexpr int KST = D + E::PAD;      // K / V tile row stride
   __shared__ __attribute__((aligned(16))) T k_lds[N * KST];
-  __shared__ __attribute__((aligned(16))) T vt_lds[D * VST];
+  __shared__ __attribute__((aligned(16))) T v_lds[N * KST];
 
   const Problem& p = args.p;
   int bg, item;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs args) {
     for (int k0 = klo; k0 < khi; k0 += N) {
       __syncthreads();
       stage_rows<T, N, D, KST>(k_lds, kbase, rs, k0, khi, tid);
-      stage_rows_t<T, N, D, VST>(vt_lds, vbase, rs, k0, khi, tid);
+      stage_rows<T, N, D, KST>(v_lds, vbase, rs, k0, khi, tid);
       __syncthreads();
       const bool need_mask = !(k0 >= flo && k0 + N <= fhi);
 
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs args) {
 #pragma unroll
         for (int cc = 0; cc < N / KC; ++cc) {
           const int sub = cc / CPS, ci = cc % CPS;
-          Frag va = ld_frag_crows<T>(vt_lds + (dt * 32 + ln) * VST + sub * 32, ci, hh);
+          Frag va = ld_frag_kcrow<T>(v_lds, KST, sub * 32, ci, lane, dt * 32);
           Frag pb = pack_frag<T>(&pv[sub][ci * KPL]);
           oacc[dt] = E::mma(va, pb, oacc[dt]);
         }
@@ -292,6 +293,130 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs args) {
 }
 
 // ======================================================= backward: main kernel
+// Per-thread register copy of one Q/dO tile slice (RPT rows x VEC columns)
+// plus the row data of row `tid` (threads < M), loaded one iteration ahead.
+template <typename T, int M, int D>
+struct BwdPrefetch {
+  static constexpr int VEC = Elt<T>::VEC;
+  static constexpr int RPT = M * D / (256 * VEC);
+  Vec16 q[RPT], d[RPT];
+  float lse2, delta;
+  int lo, hi;
+};
+
+// Iteration order of a backward workgroup: query tiles descending; at each
+// tile position the (up to two) query streams that see the key tile, then the
+// q heads of the GQA group.  Workgroups of one kv head therefore sweep the
+// same query tiles at the same time.
+// Iteration order of a backward workgroup: query tiles descending; at each
+// tile position the (up to two) query streams that see the key tile, then the
+// q heads of the GQA group.  Workgroups of one kv head therefore sweep the
+// same query tiles at the same time.  The order is a handful of uniform
+// integers: o[0..11] = s0, s1, tlo0, thi0, tlo1, thi1, inter, tb, slow,
+// nboth, n0, total.
+__device__ __forceinline__ void bwd_order(const Problem& p, int a, int ns0, int k0, int k1, int M, int* o) {
+  int s0 = 0, s1 = 0, tlo0 = 0, tlo1 = 0, thi0 = 0, thi1 = 0, nseg = 0;
+  for (int s = (a == 0 ? ns0 : 1); s < 2; ++s) {
+    if (p.rows[s] == 0) continue;
+    int rlo, rhi;
+    query_span(p, s, a, k0, k1, rlo, rhi);
+    if (rlo >= rhi) continue;
+    if (nseg == 0) { s0 = s; tlo0 = rlo / M; thi0 = (rhi - 1) / M; }
+    else { s1 = s; tlo1 = rlo / M; thi1 = (rhi - 1) / M; }
+    ++nseg;
+  }
+  const int G = p.group;
+  const int inter = (nseg == 2 && thi0 == thi1) ? 1 : 0;
+  const int tb = inter ? max(tlo0, tlo1) : 0;
+  const int nboth = inter ? (thi0 - tb + 1) * 2 * G : 0;
+  const int n0 = nseg > 0 ? (thi0 - tlo0 + 1) * G : 0;
+  o[0] = s0; o[1] = s1; o[2] = tlo0; o[3] = thi0; o[4] = tlo1; o[5] = thi1;
+  o[6] = inter; o[7] = tb; o[8] = tlo0 <= tlo1 ? s0 : s1; o[9] = nboth; o[10] = n0;
+  o[11] = inter ? nboth + (tb - min(tlo0, tlo1)) * G : n0 + (nseg > 1 ? (thi1 - tlo1 + 1) * G : 0);
+}
+
+#define BWD_DECODE(it, s, q0, h)                                   \
+  do {                                                             \
+    int t_, hg_;                                                   \
+    if (o_inter) {                                                 \
+      if ((it) < o_nboth) {                                        \
+        t_ = o_thi0 - (it) / (2 * G);                              \
+        s = (((it) / G) & 1) ? o_s1 : o_s0;                        \
+        hg_ = (it) % G;                                            \
+      } else {                                                     \
+        const int r_ = (it) - o_nboth;                             \
+        t_ = o_tb - 1 - r_ / G;                                    \
+        s = o_slow;                                                \
+        hg_ = r_ % G;                                              \
+      }                                                            \
+    } else if ((it) < o_n0) {                                      \
+      t_ = o_thi0 - (it) / G;                                      \
+      s = o_s0;                                                    \
+      hg_ = (it) % G;                                              \
+    } else {                                                       \
+      const int r_ = (it) - o_n0;                                  \
+      t_ = o_thi1 - r_ / G;                                        \
+      s = o_s1;                                                    \
+      hg_ = r_ % G;                                                \
+    }                                                              \
+    q0 = t_ * M;                                                   \
+    h = g * G + hg_;                                               \
+  } while (0)
+
+// Global -> registers: this thread's RPT x VEC slice of the Q and dO tiles of
+// (stream s, rows q0.., head h), and the row data of row `tid` (threads < M).
+template <typename T, int M, int D>
+__device__ __forceinline__ void bwd_load(const BwdArgs& args, int s, int q0, int h, int a, int b, int tid,
+                                         BwdPrefetch<T, M, D>& pf) {
+  using PF = BwdPrefetch<T, M, D>;
+  constexpr int RPT = PF::RPT, VEC = PF::VEC, RG = M / RPT;
+  const Problem& p = args.p;
+  const int R = p.rows[s];
+  const int q1 = min(q0 + M, R);
+  const int64_t qrs = (int64_t)p.hq * D;
+  const int rg = tid % RG, dcol = (tid / RG) * VEC;
+  const T* qb = reinterpret_cast<const T*>(args.q[s]) + (int64_t)b * R * qrs + (int64_t)h * D + dcol;
+  const T* db = reinterpret_cast<const T*>(args.dout[s]) + (int64_t)b * R * qrs + (int64_t)h * D + dcol;
+#pragma unroll
+  for (int jj = 0; jj < RPT; ++jj) {
+    const int r = q0 + rg * RPT + jj;
+    pf.q[jj] = r < q1 ? ld16(qb + (int64_t)r * qrs) : zero16();
+    pf.d[jj] = r < q1 ? ld16(db + (int64_t)r * qrs) : zero16();
+  }
+  if (tid < M) {
+    const int rr = q0 + tid;
+    int lo = 0, hi = 0;
+    float l2 = 0.f, dd = 0.f;
+    if (rr < q1) {
+      row_keys(p, s, rr, a, lo, hi);
+      const int64_t ri = ((int64_t)b * p.hq + h) * R + rr;
+      l2 = args.lse[s][ri] * kLog2e;
+      dd = args.delta[s][ri];
+    }
+    pf.lo = lo; pf.hi = hi; pf.lse2 = l2; pf.delta = dd;
+  }
+}
+
+// Registers -> LDS: the Q/dO slice (row-major) and the row data.
+template <typename T, int M, int D, int QST>
+__device__ __forceinline__ void bwd_store(T* q_l, T* do_l, float* lse_l, float* dl_l, int* lo_l, int* hi_l, int tid,
+                                          const BwdPrefetch<T, M, D>& pf) {
+  using PF = BwdPrefetch<T, M, D>;
+  constexpr int RPT = PF::RPT, VEC = PF::VEC, RG = M / RPT;
+  const int rg = tid % RG, dcol = (tid / RG) * VEC;
+#pragma unroll
+  for (int jj = 0; jj < RPT; ++jj) {
+    st16(q_l + (rg * RPT + jj) * QST + dcol, pf.q[jj]);
+    st16(do_l + (rg * RPT + jj) * QST + dcol, pf.d[jj]);
+  }
+  if (tid < M) {
+    lse_l[tid] = pf.lse2;
+    dl_l[tid] = pf.delta;
+    lo_l[tid] = pf.lo;
+    hi_l[tid] = pf.hi;
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
   using E = Elt<T>;
@@ -302,19 +427,20 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
   constexpr int KPL = E::KPL, KC = 2 * KPL;
   constexpr int DCH = D / KC;
   constexpr int CPS = 32 / KC;
-  constexpr int QST = D + E::PAD;      // q / dO row-major stride
-  constexpr int QTST = M + E::PAD;     // q^T / dO^T stride
-  constexpr int DSST = N + E::PAD;     // dS [query][key] stride
-  constexpr int KTST = N + E::PAD;     // K^T [d][key] stride
-  __shared__ __attribute__((aligned(16))) T q_lds[M * QST];
-  __shared__ __attribute__((aligned(16))) T do_lds[M * QST];
-  __shared__ __attribute__((aligned(16))) T qt_lds[D * QTST];
-  __shared__ __attribute__((aligned(16))) T dot_lds[D * QTST];
-  __shared__ __attribute__((aligned(16))) T ds_lds[M * DSST];
-  __shared__ __attribute__((aligned(16))) T kt_lds[D * KTST];
-  __shared__ __attribute__((aligned(16))) float lse_l[M];
-  __shared__ __attribute__((aligned(16))) float dl_l[M];
-  __shared__ int lo_l[M], hi_l[M];
+  constexpr int VEC = E::VEC;
+  constexpr int QST = D + E::PAD;      // q / dO / K row stride
+  constexpr int DTST = M + E::PAD;     // dS^T [key][query] stride
+  using PF = BwdPrefetch<T, M, D>;
+  constexpr int RPT = PF::RPT;
+  static_assert(RPT >= 1 && M * D == 256 * VEC * RPT, "tile/thread mismatch");
+  constexpr int RG = M / RPT;
+  __shared__ __attribute__((aligned(16))) T q_lds[2][M * QST];
+  __shared__ __attribute__((aligned(16))) T do_lds[2][M * QST];
+  __shared__ __attribute__((aligned(16))) T dst_lds[N * DTST];
+  __shared__ __attribute__((aligned(16))) T k_lds[N * QST];
+  __shared__ __attribute__((aligned(16))) float lse_l[2][M];
+  __shared__ __attribute__((aligned(16))) float dl_l[2][M];
+  __shared__ int lo_l[2][M], hi_l[2][M];
 
   const Problem& p = args.p;
   int bg, item;
@@ -342,130 +468,218 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
     vf[c] = ld_frag<T>(vbase + off);
     if (!kvalid) { kf[c] = Frag{}; vf[c] = Frag{}; }
   }
-  stage_rows_t<T, N, D, KTST>(kt_lds, kbase, krs, k0, k1, tid);
+  stage_rows<T, N, D, QST>(k_lds, kbase, krs, k0, k1, tid);
 
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) { dkacc[dt] = f32x16{}; dvacc[dt] = f32x16{}; }
 
+  // ---- iteration space: q tiles descending; at each tile position the
+  // streams that see this key tile, then the heads of the GQA group.  All
+  // workgroups of a kv head sweep the same query tiles at the same time.
+  int o[12];
+  bwd_order(p, a, args.ns0, k0, k1, M, o);
+  const int o_s0 = o[0], o_s1 = o[1], o_thi0 = o[3], o_thi1 = o[5], o_inter = o[6], o_tb = o[7];
+  const int o_slow = o[8], o_nboth = o[9], o_n0 = o[10], total = o[11];
+  const int G = p.group;
+  const int64_t qrs = (int64_t)p.hq * D;
+  // Pipeline of one iteration:
+  //   barrier; dQ atomics of the previous iteration; global loads of the next
+  //   Q/dO tiles into registers; S, dP, P, dS, dV, dK; barrier; dQ product
+  //   (kept in registers); next tiles -> the other LDS buffer.
+  // The atomics are issued right after the barrier so they drain while the
+  // main block runs, before the end-of-iteration wait on the tile loads.
+  PF pf;
+  if (total > 0) {
+    int s_, q0_, h_;
+    BWD_DECODE(0, s_, q0_, h_);
+    bwd_load<T, M, D>(args, s_, q0_, h_, a, b, tid, pf);
+    bwd_store<T, M, D, QST>(q_lds[0], do_lds[0], lse_l[0], dl_l[0], lo_l[0], hi_l[0], tid, pf);
+  }
   const float sl2 = args.scale_log2;
-  for (int s = (a == 0 ? args.ns0 : 1); s < 2; ++s) {
-    const int R = p.rows[s];
-    if (R == 0) continue;
-    int rlo, rhi;
-    query_span(p, s, a, k0, k1, rlo, rhi);
-    if (rlo >= rhi) continue;
-    const int64_t qrs = (int64_t)p.hq * D;
-    for (int t = (rhi - 1) / M; t >= rlo / M; --t) {
-      const int q0 = t * M;
-      const int q1 = min(q0 + M, R);
-      int klo, khi, flo, fhi;
-      tile_ranges(p, s, a, q0, q1, klo, khi, flo, fhi);
-      const bool need_mask = !(k0 >= flo && k0 + N <= fhi);
-      for (int hg = 0; hg < p.group; ++hg) {
-        const int h = g * p.group + hg;
-        const T* qb = reinterpret_cast<const T*>(args.q[s]) + (int64_t)b * R * qrs + (int64_t)h * D;
-        const T* db = reinterpret_cast<const T*>(args.dout[s]) + (int64_t)b * R * qrs + (int64_t)h * D;
-        __syncthreads();
-        stage_rows_dual<T, M, D, QST, QTST>(q_lds, qt_lds, qb, qrs, q0, q1, tid);
-        stage_rows_dual<T, M, D, QST, QTST>(do_lds, dot_lds, db, qrs, q0, q1, tid);
-        if (tid < M) {
-          const int rr = q0 + tid;
-          int lo = 0, hi = 0;
-          float l2 = 0.f, dd = 0.f;
-          if (rr < q1) {
-            row_keys(p, s, rr, a, lo, hi);
-            const int64_t ri = ((int64_t)b * p.hq + h) * R + rr;
-            l2 = args.lse[s][ri] * kLog2e;
-            dd = args.delta[s][ri];
-          }
-          lo_l[tid] = lo; hi_l[tid] = hi; lse_l[tid] = l2; dl_l[tid] = dd;
-        }
-        __syncthreads();
+  const int dq_dt = w;                       // the head_dim tile of dQ this wave owns
+  const bool dq_owner = dq_dt < D / 32;
+  f32x16 dqp[QS];                            // pending dQ tile (added one iteration later)
+  float* dqp_row = nullptr;                  // its first row pointer (lane-adjusted)
+  int dqp_rows = 0;                          // valid rows from q0 (M when full)
+  bool dqp_live = false;
 
-        // S = Q K_w^T and dP = dO V_w^T (rows = queries, column = this lane's key)
-        f32x16 sacc[QS], pacc[QS];
+  auto flush_dq = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int qs = 0; qs < QS; ++qs) {
-          sacc[qs] = f32x16{};
-          pacc[qs] = f32x16{};
+    for (int qs = 0; qs < QS; ++qs) {
+      float* rowp = dqp_row + (int64_t)(qs * 32 + 4 * hh) * qrs;
+      if (dqp_rows == M) {
 #pragma unroll
-          for (int c = 0; c < DCH; ++c) {
-            Frag qa = ld_frag<T>(q_lds + (qs * 32 + ln) * QST + c * KC + hh * KPL);
-            Frag da = ld_frag<T>(do_lds + (qs * 32 + ln) * QST + c * KC + hh * KPL);
-            sacc[qs] = E::mma(qa, kf[c], sacc[qs]);
-            pacc[qs] = E::mma(da, vf[c], pacc[qs]);
-          }
-        }
-        // P = exp(S - LSE), dS = P (dP - D)
-        float pv[QS][16], dsv[QS][16];
+        for (int i = 0; i < 16; ++i)
+          unsafeAtomicAdd(rowp + (int64_t)(((i >> 2) << 3) + (i & 3)) * qrs, dqp[qs][i] * args.scale);
+      } else {
 #pragma unroll
-        for (int qs = 0; qs < QS; ++qs) {
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int rr0 = qs * 32 + c_row(4 * i4, hh);      // 4 consecutive rows
-            const float4 l4 = *reinterpret_cast<const float4*>(lse_l + rr0);
-            const float4 d4 = *reinterpret_cast<const float4*>(dl_l + rr0);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int i = 4 * i4 + j;
-              float pe = fast_exp2(sacc[qs][i] * sl2 - lv[j]);
-              if (need_mask && !(kk >= lo_l[rr0 + j] && kk < hi_l[rr0 + j])) pe = 0.f;
-              pv[qs][i] = pe;
-              dsv[qs][i] = pe * (pacc[qs][i] - dv[j]);
-            }
-          }
-        }
-        // dV_w += P^T dO ; dK_w += dS^T Q   (k = queries in C-row order)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-          for (int cc = 0; cc < M / KC; ++cc) {
-            const int qs = cc / CPS, ci = cc % CPS;
-            Frag pa = pack_frag<T>(&pv[qs][ci * KPL]);
-            Frag sa = pack_frag<T>(&dsv[qs][ci * KPL]);
-            Frag ob = ld_frag_crows<T>(dot_lds + (dt * 32 + ln) * QTST + qs * 32, ci, hh);
-            Frag qb2 = ld_frag_crows<T>(qt_lds + (dt * 32 + ln) * QTST + qs * 32, ci, hh);
-            dvacc[dt] = E::mma(pa, ob, dvacc[dt]);
-            dkacc[dt] = E::mma(sa, qb2, dkacc[dt]);
-          }
-        }
-        // dS -> LDS as [query][key]
-#pragma unroll
-        for (int qs = 0; qs < QS; ++qs) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            ds_lds[(qs * 32 + c_row(i, hh)) * DSST + 32 * w + ln] = to_elt<T>(dsv[qs][i]);
-          }
-        }
-        __syncthreads();
-        // dQ[query][d] = dS[query][key] K[key][d], added into fp32 dQ
-        float* dqb = args.dq_acc[s] + (int64_t)b * R * qrs + (int64_t)h * D;
-        constexpr int TILES = (D / 32) * QS;
-        for (int tt = w; tt < TILES; tt += 4) {
-          const int dt = tt % (D / 32), qs = tt / (D / 32);
-          // rows = queries (A = dS from LDS), columns = head_dim (B = K^T from LDS):
-          // each lane owns one d, so an atomic instruction covers 2 x 32
-          // consecutive floats of two dQ rows.
-          f32x16 acc = f32x16{};
-#pragma unroll
-          for (int c = 0; c < N / KC; ++c) {
-            Frag sa = ld_frag<T>(ds_lds + (qs * 32 + ln) * DSST + c * KC + hh * KPL);
-            Frag kb2 = ld_frag<T>(kt_lds + (dt * 32 + ln) * KTST + c * KC + hh * KPL);
-            acc = E::mma(sa, kb2, acc);
-          }
-          float* dst = dqb + dt * 32 + ln;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rr = q0 + qs * 32 + c_row(i, hh);
-            if (rr < q1) unsafeAtomicAdd(dst + (int64_t)rr * qrs, acc[i] * args.scale);
-          }
+        for (int i = 0; i < 16; ++i) {
+          if (qs * 32 + c_row(i, hh) < dqp_rows)
+            unsafeAtomicAdd(rowp + (int64_t)(((i >> 2) << 3) + (i & 3)) * qrs, dqp[qs][i] * args.scale);
         }
       }
     }
+  };
+
+  for (int it = 0; it < total; ++it) {
+    const int cur = it & 1;
+    int s, q0, h;
+    BWD_DECODE(it, s, q0, h);
+    const int R = p.rows[s];
+    const int q1 = min(q0 + M, R);
+    int klo, khi, flo, fhi;
+    tile_ranges(p, s, a, q0, q1, klo, khi, flo, fhi);
+    const bool need_mask = !(k0 >= flo && k0 + N <= fhi);
+    __syncthreads();   // tiles of `it` are in buffer `cur`; dS^T and buffer cur^1 are free
+
+    if (dqp_live) flush_dq();
+    if (it + 1 < total) {
+      int s2, q02, h2;
+      BWD_DECODE(it + 1, s2, q02, h2);
+      bwd_load<T, M, D>(args, s2, q02, h2, a, b, tid, pf);
+    }
+    const T* qt = q_lds[cur];
+    const T* dot = do_lds[cur];
+    // One 32-row query sub-tile at a time: S = Q K_w^T and dP = dO V_w^T
+    // (rows = queries, column = this lane's key), then P and dS, then their
+    // contributions to dV_w and dK_w, then dS^T into LDS.
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      {
+        // operand fragments are read in batches of 4 k-chunks, one batch ahead
+        // of the MFMAs that consume them
+        constexpr int BT = DCH < 4 ? DCH : 4;
+        Frag qa[2][BT], da[2][BT];
+#pragma unroll
+        for (int c = 0; c < BT; ++c) {
+          qa[0][c] = ld_frag<T>(qt + (qs * 32 + ln) * QST + c * KC + hh * KPL);
+          da[0][c] = ld_frag<T>(dot + (qs * 32 + ln) * QST + c * KC + hh * KPL);
+        }
+#pragma unroll
+        for (int cb = 0; cb < DCH / BT; ++cb) {
+          if (cb + 1 < DCH / BT) {
+#pragma unroll
+            for (int c = 0; c < BT; ++c) {
+              const int cc = (cb + 1) * BT + c;
+              qa[(cb + 1) & 1][c] = ld_frag<T>(qt + (qs * 32 + ln) * QST + cc * KC + hh * KPL);
+              da[(cb + 1) & 1][c] = ld_frag<T>(dot + (qs * 32 + ln) * QST + cc * KC + hh * KPL);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < BT; ++c) {
+            sacc = E::mma(qa[cb & 1][c], kf[cb * BT + c], sacc);
+            pacc = E::mma(da[cb & 1][c], vf[cb * BT + c], pacc);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // P = exp(S - LSE), dS = P (dP - D); masked pairs get P = 0.  Both are
+      // packed into MFMA fragments right away (k = queries in C-row order).
+      Frag pfr[CPS], sfr[CPS];
+#pragma unroll
+      for (int ci = 0; ci < CPS; ++ci) {
+        float pe[KPL], de[KPL];
+#pragma unroll
+        for (int jj = 0; jj < KPL; ++jj) {
+          const int i = ci * KPL + jj;
+          const int rr = qs * 32 + c_row(i, hh);
+          float e = fast_exp2(sacc[i] * sl2 - lse_l[cur][rr]);
+          if (need_mask && !(kk >= lo_l[cur][rr] && kk < hi_l[cur][rr])) e = 0.f;
+          pe[jj] = e;
+          de[jj] = e * (pacc[i] - dl_l[cur][rr]);
+        }
+        pfr[ci] = pack_frag<T>(pe);
+        sfr[ci] = pack_frag<T>(de);
+      }
+      // dV_w += P^T dO ; dK_w += dS^T Q  (the dO / Q fragments are read
+      // transposed out of the row-major tiles)
+      {
+        // fragments of one d-tile are read while the previous d-tile's MFMAs run
+        Frag ob[2][CPS], qb2[2][CPS];
+#pragma unroll
+        for (int ci = 0; ci < CPS; ++ci) {
+          ob[0][ci] = ld_frag_kcrow<T>(dot, QST, qs * 32, ci, lane, 0);
+          qb2[0][ci] = ld_frag_kcrow<T>(qt, QST, qs * 32, ci, lane, 0);
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          if (dt + 1 < D / 32) {
+#pragma unroll
+            for (int ci = 0; ci < CPS; ++ci) {
+              ob[(dt + 1) & 1][ci] = ld_frag_kcrow<T>(dot, QST, qs * 32, ci, lane, (dt + 1) * 32);
+              qb2[(dt + 1) & 1][ci] = ld_frag_kcrow<T>(qt, QST, qs * 32, ci, lane, (dt + 1) * 32);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ci = 0; ci < CPS; ++ci) {
+            dvacc[dt] = E::mma(pfr[ci], ob[dt & 1][ci], dvacc[dt]);
+            dkacc[dt] = E::mma(sfr[ci], qb2[dt & 1][ci], dkacc[dt]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // dS^T -> LDS as [key][query]: runs of 4 consecutive queries per write
+#pragma unroll
+      for (int ci = 0; ci < CPS; ++ci)
+        store_crow_run<T>(dst_lds + (32 * w + ln) * DTST + qs * 32, ci, hh, sfr[ci]);
+    }
+    __syncthreads();   // dS^T complete
+
+    // dQ[query][d] = dS[query][key] K[key][d] for this wave's head_dim tile.
+    // Rows = queries (A = dS, read transposed out of dS^T), columns = head_dim
+    // (B = K read transposed out of the row-major K tile), so each later atomic
+    // instruction covers 2 x 32 consecutive floats of two dQ rows.
+    dqp_live = false;
+    if (dq_owner) {
+      const int dt = dq_dt;
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) dqp[qs] = f32x16{};
+      {
+        constexpr int NC = N / KC;
+        constexpr int BT = NC < 2 ? NC : 2;
+        Frag kb2[2][BT], sa[2][BT][QS];
+#pragma unroll
+        for (int c = 0; c < BT; ++c) {
+          kb2[0][c] = ld_frag_knat<T>(k_lds, QST, c * KC, lane, dt * 32);
+#pragma unroll
+          for (int qs = 0; qs < QS; ++qs) sa[0][c][qs] = ld_frag_knat<T>(dst_lds, DTST, c * KC, lane, qs * 32);
+        }
+#pragma unroll
+        for (int cb = 0; cb < NC / BT; ++cb) {
+          if (cb + 1 < NC / BT) {
+#pragma unroll
+            for (int c = 0; c < BT; ++c) {
+              const int cc = (cb + 1) * BT + c;
+              kb2[(cb + 1) & 1][c] = ld_frag_knat<T>(k_lds, QST, cc * KC, lane, dt * 32);
+#pragma unroll
+              for (int qs = 0; qs < QS; ++qs)
+                sa[(cb + 1) & 1][c][qs] = ld_frag_knat<T>(dst_lds, DTST, cc * KC, lane, qs * 32);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < BT; ++c) {
+#pragma unroll
+            for (int qs = 0; qs < QS; ++qs) dqp[qs] = E::mma(sa[cb & 1][c][qs], kb2[cb & 1][c], dqp[qs]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      dqp_row = args.dq_acc[s] + (int64_t)b * R * qrs + (int64_t)h * D + (int64_t)q0 * qrs + dt * 32 + ln;
+      dqp_rows = q1 - q0;
+      dqp_live = true;
+    }
+    // next tiles into the other buffer (its last reader finished before this
+    // iteration's first barrier)
+    if (it + 1 < total)
+      bwd_store<T, M, D, QST>(q_lds[cur ^ 1], do_lds[cur ^ 1], lse_l[cur ^ 1], dl_l[cur ^ 1], lo_l[cur ^ 1],
+                              hi_l[cur ^ 1], tid, pf);
   }
+  if (dqp_live) flush_dq();
 
   // dK = scale * sum dS^T Q, dV = sum P^T dO for the wave's 32 keys.
   T* dkb = reinterpret_cast<T*>(args.dk[a]) + (int64_t)b * p.klen[a] * krs + (int64_t)g * D;
