@@ -118,7 +118,8 @@ int bdlm_attn_fwd(const bdlm_attn_desc* desc,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Backward with the stored-LSE recompute (P is rebuilt from Q, K and LSE).
+ * Backward with the stored-LSE recompute (P is rebuilt from Q, K and LSE):
+ * D = rowsum(dO * O), then dK/dV key-major and dQ query-major (no atomics).
  * Full mode: inputs as the forward plus its outputs oc, ox, lse_c, lse_x and the
  *   upstream gradients doc, dox [batch, L, Hq, d].  Overwrites dqc, dqx
  *   [batch, L, Hq, d] and dkc, dvc, dkx, dvx [batch, L, Hkv, d] (all dtype).
@@ -158,8 +159,9 @@ int bdlm_attn_merge_partials(int32_t num_parts, int32_t batch, int64_t tokens,
                              hipStream_t stream);
 
 /*
- * Diagnostics: walk the forward (for_bwd = 0) or backward (for_bwd = 1) work
- * decomposition on the host exactly as the kernels traverse it, for batch 0 and
+ * Diagnostics: walk a kernel's work decomposition on the host exactly as the
+ * kernel traverses it -- for_bwd = 0: forward, 1: backward dK/dV (key-major),
+ * 2: backward dQ (query-major, the forward's decomposition) -- for batch 0 and
  * q-head 0, adding 1 to cover[row * keys + key] (saturating at 255) for every
  * (query row, key) pair the kernels treat as visible.  Rows are the query rows
  * of stream 0 followed by stream 1 (full mode: 2L rows; share mode: 0 + n*B);

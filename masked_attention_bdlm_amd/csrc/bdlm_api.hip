@@ -107,21 +107,19 @@ XcdMap make_map(int nbg, int per_bg) {
 
 size_t elt_size(int dtype) { return dtype == BDLM_BF16 ? 2 : 4; }
 
-struct BwdLayout { size_t delta_off[2], dq_off[2], total; };
+struct BwdLayout { size_t delta_off[2], total; };
 
 BwdLayout bwd_layout(const bdlm_attn_desc* d) {
   BwdLayout l{};
-  const int64_t B = d->batch, H = d->num_q_heads, D = d->head_dim;
+  const int64_t B = d->batch, H = d->num_q_heads;
   size_t off = 0;
   if (d->num_local_blocks == 0) {
     const int64_t L = d->seqlen;
     for (int s = 0; s < 2; ++s) { l.delta_off[s] = off; off = align256(off + sizeof(float) * B * H * L); }
-    for (int s = 0; s < 2; ++s) { l.dq_off[s] = off; off = align256(off + sizeof(float) * B * L * H * D); }
   } else {
     const int64_t T = (int64_t)d->num_local_blocks * d->block;
     l.delta_off[0] = l.delta_off[1] = off;
     off = align256(off + sizeof(float) * B * H * T);
-    l.dq_off[0] = l.dq_off[1] = 0;
   }
   l.total = off;
   return l;
@@ -219,71 +217,81 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   const Problem p = make_problem(desc);
   char* wsb = reinterpret_cast<char*>(ws);
   float* delta[2] = {reinterpret_cast<float*>(wsb + lay.delta_off[0]), reinterpret_cast<float*>(wsb + lay.delta_off[1])};
-  float* dqacc[2];
-  if (share) {
-    dqacc[0] = nullptr;
-    dqacc[1] = reinterpret_cast<float*>(dqx);
-  } else {
-    dqacc[0] = reinterpret_cast<float*>(wsb + lay.dq_off[0]);
-    dqacc[1] = reinterpret_cast<float*>(wsb + lay.dq_off[1]);
-  }
+  const int nbg = p.batch * p.hkv;
 
-  // 1) D = rowsum(dO * O), zero the dQ accumulators (full mode)
+  // 1) D = rowsum(dO * O)
   const void* os[2] = {oc, ox};
   const void* dos[2] = {doc, dox};
   for (int s = share ? 1 : 0; s < 2; ++s) {
     BwdPreArgs pa;
     pa.batch = p.batch; pa.rows = p.rows[s]; pa.hq = p.hq; pa.D = p.D; pa.stream = s;
     pa.o = os[s]; pa.dout = dos[s]; pa.delta = delta[s];
-    pa.dq_acc = share ? nullptr : dqacc[s];
+    pa.dq_acc = nullptr;
     ProfScope ps("bdlm_bwd_pre", stream);
     if (launch_bwd_pre(pa, bf, stream) != hipSuccess) return BDLM_ERR_HIP;
   }
 
-  // 2) KV-major main kernel
-  BwdArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.p = p;
-  a.q[0] = qc; a.q[1] = qx;
-  a.k[0] = kc; a.k[1] = kx;
-  a.v[0] = vc; a.v[1] = vx;
-  a.dout[0] = doc; a.dout[1] = dox;
-  a.lse[0] = lse_c; a.lse[1] = lse_x;
-  a.delta[0] = delta[0]; a.delta[1] = delta[1];
-  a.dq_acc[0] = dqacc[0]; a.dq_acc[1] = dqacc[1];
-  a.dk[0] = dkc; a.dk[1] = dkx;
-  a.dv[0] = dvc; a.dv[1] = dvx;
-  a.scale = desc->softmax_scale;
-  a.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
-  a.ns0 = share ? 1 : 0;
-  if (share) {
-    a.kbase[0] = p.kv_begin; a.kend[0] = p.kv_end;
-    a.nkt[0] = (p.kv_end - p.kv_begin + kBwdTileN - 1) / kBwdTileN;
-    a.kbase[1] = 0; a.kend[1] = p.klen[1];
-    a.nkt[1] = p.own_block ? (p.klen[1] + kBwdTileN - 1) / kBwdTileN : 0;
-  } else {
-    for (int k = 0; k < 2; ++k) {
-      a.kbase[k] = 0; a.kend[k] = p.L;
-      a.nkt[k] = (p.L + kBwdTileN - 1) / kBwdTileN;
+  // 2) dK, dV: key-major
+  {
+    BwdArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.p = p;
+    a.q[0] = qc; a.q[1] = qx;
+    a.k[0] = kc; a.k[1] = kx;
+    a.v[0] = vc; a.v[1] = vx;
+    a.dout[0] = doc; a.dout[1] = dox;
+    a.lse[0] = lse_c; a.lse[1] = lse_x;
+    a.delta[0] = delta[0]; a.delta[1] = delta[1];
+    a.dk[0] = dkc; a.dk[1] = dkx;
+    a.dv[0] = dvc; a.dv[1] = dvx;
+    a.scale = desc->softmax_scale;
+    a.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
+    a.ns0 = share ? 1 : 0;
+    if (share) {
+      a.kbase[0] = p.kv_begin; a.kend[0] = p.kv_end;
+      a.nkt[0] = (p.kv_end - p.kv_begin + kBwdTileN - 1) / kBwdTileN;
+      a.kbase[1] = 0; a.kend[1] = p.klen[1];
+      a.nkt[1] = p.own_block ? (p.klen[1] + kBwdTileN - 1) / kBwdTileN : 0;
+    } else {
+      for (int k = 0; k < 2; ++k) {
+        a.kbase[k] = 0; a.kend[k] = p.L;
+        a.nkt[k] = (p.L + kBwdTileN - 1) / kBwdTileN;
+      }
+    }
+    const int per_bg = a.nkt[0] + a.nkt[1];
+    a.map = make_map(nbg, per_bg);
+    const int64_t grid = (int64_t)nbg * per_bg;
+    if (grid > 0x7fffffff) return BDLM_ERR_UNSUPPORTED;
+    if (grid > 0) {
+      ProfScope ps("bdlm_dkdv", stream);
+      if (launch_dkdv(a, (int)grid, bf, stream) != hipSuccess) return BDLM_ERR_HIP;
     }
   }
-  const int per_bg = a.nkt[0] + a.nkt[1];
-  const int nbg = p.batch * p.hkv;
-  a.map = make_map(nbg, per_bg);
-  const int64_t grid = (int64_t)nbg * per_bg;
-  if (grid > 0x7fffffff) return BDLM_ERR_UNSUPPORTED;
-  if (grid > 0) {
-    ProfScope ps("bdlm_bwd", stream);
-    if (launch_bwd(a, (int)grid, bf, stream) != hipSuccess) return BDLM_ERR_HIP;
-  }
 
-  // 3) dQ fp32 -> dtype (full mode)
-  if (!share) {
-    void* dqs[2] = {dqc, dqx};
-    for (int s = 0; s < 2; ++s) {
-      ProfScope ps("bdlm_bwd_post", stream);
-      const int64_t n = (int64_t)p.batch * p.L * p.hq * p.D;
-      if (launch_convert(dqacc[s], dqs[s], n, bf, stream) != hipSuccess) return BDLM_ERR_HIP;
+  // 3) dQ: query-major, no atomics (share mode adds into the fp32 dqx)
+  {
+    DqArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.p = p;
+    a.q[0] = qc; a.q[1] = qx;
+    a.k[0] = kc; a.k[1] = kx;
+    a.v[0] = vc; a.v[1] = vx;
+    a.dout[0] = doc; a.dout[1] = dox;
+    a.lse[0] = lse_c; a.lse[1] = lse_x;
+    a.delta[0] = delta[0]; a.delta[1] = delta[1];
+    a.dq[0] = dqc; a.dq[1] = dqx;
+    a.scale = desc->softmax_scale;
+    a.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
+    a.ns0 = share ? 1 : 0;
+    for (int s = 0; s < 2; ++s) a.nqt[s] = (p.rows[s] + kFwdTileM - 1) / kFwdTileM;
+    const int nstr = 2 - a.ns0;
+    const int per_bg = a.nqt[1] * nstr * p.group;
+    a.map = make_map(nbg, per_bg);
+    const int64_t grid = (int64_t)nbg * per_bg;
+    if (grid > 0x7fffffff) return BDLM_ERR_UNSUPPORTED;
+    if (grid > 0) {
+      ProfScope ps("bdlm_dq", stream);
+      if (launch_dq(a, (int)grid, bf, share ? 1 : 0, stream) != hipSuccess) return BDLM_ERR_HIP;
     }
   }
   return BDLM_OK;
@@ -321,6 +329,7 @@ int bdlm_attn_schedule_walk(const bdlm_attn_desc* desc, int for_bwd, uint8_t* co
                             int64_t* stats) {
   int st = check_desc(desc);
   if (st != BDLM_OK) return st;
+  if (for_bwd < 0 || for_bwd > 2) return BDLM_ERR_INVALID_ARG;
   const Problem p = make_problem(desc);
   const int64_t nrows = (int64_t)p.rows[0] + p.rows[1];
   const int64_t nkeys = (int64_t)p.klen[0] + p.klen[1];
@@ -337,7 +346,7 @@ int bdlm_attn_schedule_walk(const bdlm_attn_desc* desc, int for_bwd, uint8_t* co
     }
   };
   const int nbg = p.batch * p.hkv;
-  if (!for_bwd) {
+  if (for_bwd != 1) {   // forward and dQ kernels share the query-major decomposition
     const int ns0 = p.mode == 0 ? 0 : 1, nstr = 2 - ns0;
     int nqt[2];
     for (int s = 0; s < 2; ++s) nqt[s] = (p.rows[s] + kFwdTileM - 1) / kFwdTileM;

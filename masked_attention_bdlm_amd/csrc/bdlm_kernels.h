@@ -37,13 +37,27 @@ struct BwdArgs {
   const void* dout[2];
   const float* lse[2];
   const float* delta[2];
-  float* dq_acc[2];     // fp32 [batch, rows, hq, D]
   void* dk[2];
   void* dv[2];
   float scale, scale_log2;
   int nkt[2];           // 128-key tiles per key array
   int kbase[2];         // first key of tile 0
   int kend[2];          // one past the last key
+  int ns0;
+  XcdMap map;
+};
+
+struct DqArgs {
+  Problem p;
+  const void* q[2];
+  const void* k[2];
+  const void* v[2];
+  const void* dout[2];
+  const float* lse[2];
+  const float* delta[2];
+  void* dq[2];          // dtype (full mode) or fp32 to add into (share mode)
+  float scale, scale_log2;
+  int nqt[2];           // 128-row query tiles per stream
   int ns0;
   XcdMap map;
 };
@@ -63,7 +77,8 @@ constexpr int kBwdTileN = 128;
 
 hipError_t launch_fwd(const FwdArgs& a, int grid, int is_bf16, int out_f32, hipStream_t st);
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t st);
-hipError_t launch_bwd(const BwdArgs& a, int grid, int is_bf16, hipStream_t st);
+hipError_t launch_dkdv(const BwdArgs& a, int grid, int is_bf16, hipStream_t st);
+hipError_t launch_dq(const DqArgs& a, int grid, int is_bf16, int add_f32, hipStream_t st);
 hipError_t launch_convert(const float* src, void* dst, int64_t n, int is_bf16, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int out_bf16, hipStream_t st);
 

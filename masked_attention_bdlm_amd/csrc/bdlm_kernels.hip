@@ -418,7 +418,7 @@ __device__ __forceinline__ void bwd_store(T* q_l, T* do_l, float* lse_l, float* 
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
   using E = Elt<T>;
   using Frag = typename E::Frag;
   constexpr int N = 128;                                   // keys per workgroup
@@ -429,15 +429,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
   constexpr int CPS = 32 / KC;
   constexpr int VEC = E::VEC;
   constexpr int QST = D + E::PAD;      // q / dO / K row stride
-  constexpr int DTST = M + E::PAD;     // dS^T [key][query] stride
   using PF = BwdPrefetch<T, M, D>;
   constexpr int RPT = PF::RPT;
   static_assert(RPT >= 1 && M * D == 256 * VEC * RPT, "tile/thread mismatch");
   constexpr int RG = M / RPT;
   __shared__ __attribute__((aligned(16))) T q_lds[2][M * QST];
   __shared__ __attribute__((aligned(16))) T do_lds[2][M * QST];
-  __shared__ __attribute__((aligned(16))) T dst_lds[N * DTST];
-  __shared__ __attribute__((aligned(16))) T k_lds[N * QST];
   __shared__ __attribute__((aligned(16))) float lse_l[2][M];
   __shared__ __attribute__((aligned(16))) float dl_l[2][M];
   __shared__ int lo_l[2][M], hi_l[2][M];
@@ -468,8 +465,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
     vf[c] = ld_frag<T>(vbase + off);
     if (!kvalid) { kf[c] = Frag{}; vf[c] = Frag{}; }
   }
-  stage_rows<T, N, D, QST>(k_lds, kbase, krs, k0, k1, tid);
-
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) { dkacc[dt] = f32x16{}; dvacc[dt] = f32x16{}; }
@@ -482,13 +477,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
   const int o_s0 = o[0], o_s1 = o[1], o_thi0 = o[3], o_thi1 = o[5], o_inter = o[6], o_tb = o[7];
   const int o_slow = o[8], o_nboth = o[9], o_n0 = o[10], total = o[11];
   const int G = p.group;
-  const int64_t qrs = (int64_t)p.hq * D;
-  // Pipeline of one iteration:
-  //   barrier; dQ atomics of the previous iteration; global loads of the next
-  //   Q/dO tiles into registers; S, dP, P, dS, dV, dK; barrier; dQ product
-  //   (kept in registers); next tiles -> the other LDS buffer.
-  // The atomics are issued right after the barrier so they drain while the
-  // main block runs, before the end-of-iteration wait on the tile loads.
+  // One barrier per iteration: after it, tiles of `it` are in buffer `cur`
+  // and every wave has finished reading buffer cur^1; the loads of the next
+  // tiles are issued into registers, the main block runs, and the next tiles
+  // are written into buffer cur^1 at the end.
   PF pf;
   if (total > 0) {
     int s_, q0_, h_;
@@ -497,31 +489,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
     bwd_store<T, M, D, QST>(q_lds[0], do_lds[0], lse_l[0], dl_l[0], lo_l[0], hi_l[0], tid, pf);
   }
   const float sl2 = args.scale_log2;
-  const int dq_dt = w;                       // the head_dim tile of dQ this wave owns
-  const bool dq_owner = dq_dt < D / 32;
-  f32x16 dqp[QS];                            // pending dQ tile (added one iteration later)
-  float* dqp_row = nullptr;                  // its first row pointer (lane-adjusted)
-  int dqp_rows = 0;                          // valid rows from q0 (M when full)
-  bool dqp_live = false;
-
-  auto flush_dq = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      float* rowp = dqp_row + (int64_t)(qs * 32 + 4 * hh) * qrs;
-      if (dqp_rows == M) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          unsafeAtomicAdd(rowp + (int64_t)(((i >> 2) << 3) + (i & 3)) * qrs, dqp[qs][i] * args.scale);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (qs * 32 + c_row(i, hh) < dqp_rows)
-            unsafeAtomicAdd(rowp + (int64_t)(((i >> 2) << 3) + (i & 3)) * qrs, dqp[qs][i] * args.scale);
-        }
-      }
-    }
-  };
-
   for (int it = 0; it < total; ++it) {
     const int cur = it & 1;
     int s, q0, h;
@@ -531,9 +498,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
     int klo, khi, flo, fhi;
     tile_ranges(p, s, a, q0, q1, klo, khi, flo, fhi);
     const bool need_mask = !(k0 >= flo && k0 + N <= fhi);
-    __syncthreads();   // tiles of `it` are in buffer `cur`; dS^T and buffer cur^1 are free
-
-    if (dqp_live) flush_dq();
+    __syncthreads();
     if (it + 1 < total) {
       int s2, q02, h2;
       BWD_DECODE(it + 1, s2, q02, h2);
@@ -622,64 +587,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // dS^T -> LDS as [key][query]: runs of 4 consecutive queries per write
-#pragma unroll
-      for (int ci = 0; ci < CPS; ++ci)
-        store_crow_run<T>(dst_lds + (32 * w + ln) * DTST + qs * 32, ci, hh, sfr[ci]);
     }
-    __syncthreads();   // dS^T complete
-
-    // dQ[query][d] = dS[query][key] K[key][d] for this wave's head_dim tile.
-    // Rows = queries (A = dS, read transposed out of dS^T), columns = head_dim
-    // (B = K read transposed out of the row-major K tile), so each later atomic
-    // instruction covers 2 x 32 consecutive floats of two dQ rows.
-    dqp_live = false;
-    if (dq_owner) {
-      const int dt = dq_dt;
-#pragma unroll
-      for (int qs = 0; qs < QS; ++qs) dqp[qs] = f32x16{};
-      {
-        constexpr int NC = N / KC;
-        constexpr int BT = NC < 2 ? NC : 2;
-        Frag kb2[2][BT], sa[2][BT][QS];
-#pragma unroll
-        for (int c = 0; c < BT; ++c) {
-          kb2[0][c] = ld_frag_knat<T>(k_lds, QST, c * KC, lane, dt * 32);
-#pragma unroll
-          for (int qs = 0; qs < QS; ++qs) sa[0][c][qs] = ld_frag_knat<T>(dst_lds, DTST, c * KC, lane, qs * 32);
-        }
-#pragma unroll
-        for (int cb = 0; cb < NC / BT; ++cb) {
-          if (cb + 1 < NC / BT) {
-#pragma unroll
-            for (int c = 0; c < BT; ++c) {
-              const int cc = (cb + 1) * BT + c;
-              kb2[(cb + 1) & 1][c] = ld_frag_knat<T>(k_lds, QST, cc * KC, lane, dt * 32);
-#pragma unroll
-              for (int qs = 0; qs < QS; ++qs)
-                sa[(cb + 1) & 1][c][qs] = ld_frag_knat<T>(dst_lds, DTST, cc * KC, lane, qs * 32);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int c = 0; c < BT; ++c) {
-#pragma unroll
-            for (int qs = 0; qs < QS; ++qs) dqp[qs] = E::mma(sa[cb & 1][c][qs], kb2[cb & 1][c], dqp[qs]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      dqp_row = args.dq_acc[s] + (int64_t)b * R * qrs + (int64_t)h * D + (int64_t)q0 * qrs + dt * 32 + ln;
-      dqp_rows = q1 - q0;
-      dqp_live = true;
-    }
-    // next tiles into the other buffer (its last reader finished before this
-    // iteration's first barrier)
     if (it + 1 < total)
       bwd_store<T, M, D, QST>(q_lds[cur ^ 1], do_lds[cur ^ 1], lse_l[cur ^ 1], dl_l[cur ^ 1], lo_l[cur ^ 1],
                               hi_l[cur ^ 1], tid, pf);
   }
-  if (dqp_live) flush_dq();
 
   // dK = scale * sum dS^T Q, dV = sum P^T dO for the wave's 32 keys.
   T* dkb = reinterpret_cast<T*>(args.dk[a]) + (int64_t)b * p.klen[a] * krs + (int64_t)g * D;
@@ -695,6 +607,186 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs args) {
         dvb[off] = to_elt<T>(dvacc[dt][i]);
       }
     }
+  }
+}
+
+// ======================================================== backward: dQ kernel
+// Query-major: one workgroup per (batch, q-head, stream, 128-row query tile),
+// the forward's decomposition.  Per key tile it recomputes S^T = K Q^T and
+// dP^T = V dO^T (lane = query), forms dS^T = P^T (dP^T - D) with
+// P^T = exp(S^T - LSE) in registers, and accumulates dQ^T += K^T dS^T with dS^T
+// as the MFMA B operand straight from registers and K^T read transposed out of
+// the row-major K tile.  Each dQ row is written once: no atomics.
+template <typename T, int D, bool ADD_F32>
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs args) {
+  using E = Elt<T>;
+  using Frag = typename E::Frag;
+  constexpr int M = 128, N = 64;
+  constexpr int KPL = E::KPL, KC = 2 * KPL;
+  constexpr int DCH = D / KC;
+  constexpr int CPS = 32 / KC;
+  constexpr int KST = D + E::PAD;
+  __shared__ __attribute__((aligned(16))) T k_lds[N * KST];
+  __shared__ __attribute__((aligned(16))) T v_lds[N * KST];
+
+  const Problem& p = args.p;
+  int bg, item;
+  args.map.decode(blockIdx.x, bg, item);
+  const int b = bg / p.hkv, g = bg % p.hkv;
+  const int hg = item % p.group;
+  const int rest = item / p.group;
+  const int nstr = 2 - args.ns0;
+  const int s = args.ns0 + rest % nstr;
+  const int t = args.nqt[s] - 1 - rest / nstr;
+  const int h = g * p.group + hg;
+  const int R = p.rows[s];
+  const int r0 = t * M;
+  const int r1 = min(r0 + M, R);
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int ln = lane & 31, hh = lane >> 5;
+  const int r = r0 + 32 * w + ln;
+  const bool valid = r < r1;
+  const int64_t qrs = (int64_t)p.hq * D;
+
+  // Q^T and dO^T fragments (MFMA B operands): column = this lane's query.
+  Frag qf[DCH], df[DCH];
+  {
+    const int64_t off = ((int64_t)b * R + (valid ? r : r0)) * qrs + (int64_t)h * D + hh * KPL;
+    const T* qrow = reinterpret_cast<const T*>(args.q[s]) + off;
+    const T* drow = reinterpret_cast<const T*>(args.dout[s]) + off;
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) {
+      qf[c] = ld_frag<T>(qrow + c * KC);
+      df[c] = ld_frag<T>(drow + c * KC);
+      if (!valid) { qf[c] = Frag{}; df[c] = Frag{}; }
+    }
+  }
+  float lse2 = 0.f, dd = 0.f;
+  if (valid) {
+    const int64_t ri = ((int64_t)b * p.hq + h) * R + r;
+    lse2 = args.lse[s][ri] * kLog2e;
+    dd = args.delta[s][ri];
+  }
+  int lo[2], hi[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    if (valid) row_keys(p, s, r, a, lo[a], hi[a]); else lo[a] = hi[a] = 0;
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  bool any = false;
+
+  for (int a = 0; a < 2; ++a) {
+    int klo, khi, flo, fhi;
+    tile_ranges(p, s, a, r0, r1, klo, khi, flo, fhi);
+    if (klo >= khi) continue;
+    any = true;
+    const int64_t rs = (int64_t)p.hkv * D;
+    const T* kbase = reinterpret_cast<const T*>(args.k[a]) + (int64_t)b * p.klen[a] * rs + (int64_t)g * D;
+    const T* vbase = reinterpret_cast<const T*>(args.v[a]) + (int64_t)b * p.klen[a] * rs + (int64_t)g * D;
+    const int mylo = lo[a], myhi = hi[a];
+
+    for (int k0 = klo; k0 < khi; k0 += N) {
+      __syncthreads();
+      stage_rows<T, N, D, KST>(k_lds, kbase, rs, k0, khi, tid);
+      stage_rows<T, N, D, KST>(v_lds, vbase, rs, k0, khi, tid);
+      __syncthreads();
+      const bool need_mask = !(k0 >= flo && k0 + N <= fhi) || (r1 - r0 < M);
+
+      // per 32-key sub-tile: S^T = K Q^T and dP^T = V dO^T, then
+      // dS^T = P^T (dP^T - D) with P^T = exp(S^T - LSE), then dQ^T += K^T dS^T
+#pragma unroll
+      for (int sub = 0; sub < N / 32; ++sub) {
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
+        {
+          constexpr int BT = DCH < 4 ? DCH : 4;
+          Frag ka[2][BT], va[2][BT];
+#pragma unroll
+          for (int c = 0; c < BT; ++c) {
+            ka[0][c] = ld_frag<T>(k_lds + (sub * 32 + ln) * KST + c * KC + hh * KPL);
+            va[0][c] = ld_frag<T>(v_lds + (sub * 32 + ln) * KST + c * KC + hh * KPL);
+          }
+#pragma unroll
+          for (int cb = 0; cb < DCH / BT; ++cb) {
+            if (cb + 1 < DCH / BT) {
+#pragma unroll
+              for (int c = 0; c < BT; ++c) {
+                const int cc = (cb + 1) * BT + c;
+                ka[(cb + 1) & 1][c] = ld_frag<T>(k_lds + (sub * 32 + ln) * KST + cc * KC + hh * KPL);
+                va[(cb + 1) & 1][c] = ld_frag<T>(v_lds + (sub * 32 + ln) * KST + cc * KC + hh * KPL);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int c = 0; c < BT; ++c) {
+              sacc = E::mma(ka[cb & 1][c], qf[cb * BT + c], sacc);
+              pacc = E::mma(va[cb & 1][c], df[cb * BT + c], pacc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        Frag dsf[CPS];
+#pragma unroll
+        for (int ci = 0; ci < CPS; ++ci) {
+          float de[KPL];
+#pragma unroll
+          for (int jj = 0; jj < KPL; ++jj) {
+            const int i = ci * KPL + jj;
+            float e = fast_exp2(sacc[i] * args.scale_log2 - lse2);
+            if (need_mask) {
+              const int kk = k0 + sub * 32 + c_row(i, hh);
+              if (kk < mylo || kk >= myhi) e = 0.f;
+            }
+            de[jj] = e * (pacc[i] - dd);
+          }
+          dsf[ci] = pack_frag<T>(de);
+        }
+        // dQ^T[d][query] += K^T[d][key] dS^T[key][query]
+        {
+          Frag kt[2][CPS];
+#pragma unroll
+          for (int ci = 0; ci < CPS; ++ci) kt[0][ci] = ld_frag_kcrow<T>(k_lds, KST, sub * 32, ci, lane, 0);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            if (dt + 1 < D / 32) {
+#pragma unroll
+              for (int ci = 0; ci < CPS; ++ci)
+                kt[(dt + 1) & 1][ci] = ld_frag_kcrow<T>(k_lds, KST, sub * 32, ci, lane, (dt + 1) * 32);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ci = 0; ci < CPS; ++ci) acc[dt] = E::mma(kt[dt & 1][ci], dsf[ci], acc[dt]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+  }
+
+  if (valid && any) {
+    using OT = typename std::conditional<ADD_F32, float, T>::type;
+    OT* orow = reinterpret_cast<OT*>(args.dq[s]) + ((int64_t)b * R + r) * qrs + (int64_t)h * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        OT* dst = orow + dt * 32 + g4 * 8 + hh * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = acc[dt][g4 * 4 + j] * args.scale;
+          if (ADD_F32) dst[j] = static_cast<OT>(static_cast<float>(dst[j]) + v);
+          else dst[j] = static_cast<OT>(v);
+        }
+      }
+    }
+  } else if (valid && !ADD_F32) {
+    // a row that sees no key in full mode cannot exist; keep the output defined
+    using OT = typename std::conditional<ADD_F32, float, T>::type;
+    OT* orow = reinterpret_cast<OT*>(args.dq[s]) + ((int64_t)b * R + r) * qrs + (int64_t)h * D;
+    for (int d = hh; d < D; d += 2) orow[d] = static_cast<OT>(0.f);
   }
 }
 
@@ -791,16 +883,29 @@ hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int grid, int is_bf16, hipStream_t st) {
+hipError_t launch_dkdv(const BwdArgs& a, int grid, int is_bf16, hipStream_t st) {
   const int D = a.p.D;
   if (is_bf16) {
-    if (D == 128) hipLaunchKernelGGL((bwd_kernel<bf16, 128>), dim3(grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((bwd_kernel<bf16, 64>), dim3(grid), dim3(256), 0, st, a);
+    if (D == 128) hipLaunchKernelGGL((dkdv_kernel<bf16, 128>), dim3(grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dkdv_kernel<bf16, 64>), dim3(grid), dim3(256), 0, st, a);
   } else {
-    if (D == 128) hipLaunchKernelGGL((bwd_kernel<float, 128>), dim3(grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((bwd_kernel<float, 64>), dim3(grid), dim3(256), 0, st, a);
+    if (D == 128) hipLaunchKernelGGL((dkdv_kernel<float, 128>), dim3(grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dkdv_kernel<float, 64>), dim3(grid), dim3(256), 0, st, a);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_dq_t(const DqArgs& a, int grid, int add_f32, hipStream_t st) {
+  if (add_f32) hipLaunchKernelGGL((dq_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((dq_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq(const DqArgs& a, int grid, int is_bf16, int add_f32, hipStream_t st) {
+  const int D = a.p.D;
+  if (is_bf16) return D == 128 ? launch_dq_t<bf16, 128>(a, grid, add_f32, st) : launch_dq_t<bf16, 64>(a, grid, add_f32, st);
+  return D == 128 ? launch_dq_t<float, 128>(a, grid, add_f32, st) : launch_dq_t<float, 64>(a, grid, add_f32, st);
 }
 
 hipError_t launch_convert(const float* src, void* dst, int64_t n, int is_bf16, hipStream_t st) {
