@@ -132,6 +132,77 @@ template <> __device__ inline float ld_frag_knat<float>(const float* tile, int s
   return tile[(row0 + (lane >> 5)) * stride + col0 + (lane & 31)];
 }
 
+// ---- unpadded row-major tiles with XOR-swizzled 16-byte chunks
+//
+// Row r of a D-column tile is D*sizeof(T) bytes = CH chunks of 16 bytes;
+// logical chunk c of row r is stored at chunk c ^ (r % CH).  A 16-lane read of
+// one logical chunk from 16 consecutive rows, and a transpose read of 4 rows,
+// both land on distinct LDS banks, and a row block of 1 KB is contiguous, so a
+// wave's global->LDS DMA (64 lanes x 16 bytes) fills 64/CH whole rows.
+template <typename T, int D>
+struct Swz {
+  static constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
+  static constexpr int CH = D / EPC;                // chunks per row
+  static constexpr int RPB = 64 / CH;               // rows per 1 KB DMA block
+  __device__ static inline int idx(int r, int col) {
+    return r * D + ((((col / EPC) ^ (r & (CH - 1)))) * EPC) + (col % EPC);
+  }
+};
+
+template <typename T, int D> __device__ inline typename Elt<T>::Frag ld_frag_s(const T* tile, int r, int col) {
+  return ld_frag<T>(tile + Swz<T, D>::idx(r, col));
+}
+
+template <int D> __device__ inline bf16x4 ld_tr4_s(const bf16* tile, int r0, int c0, int i16) {
+  const bf16* p = tile + Swz<bf16, D>::idx(r0 + (i16 >> 2), c0 + 4 * (i16 & 3));
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// ld_frag_kcrow / ld_frag_knat on a swizzled tile.
+template <typename T, int D> __device__ inline typename Elt<T>::Frag ld_frag_kcrow_s(const T* tile, int row0, int ci,
+                                                                                   int lane, int col0);
+template <> __device__ inline bf16x8 ld_frag_kcrow_s<bf16, 128>(const bf16* tile, int row0, int ci, int lane, int col0) {
+  const int r = row0 + 16 * ci + 4 * (lane >> 5), c = col0 + ((lane >> 4) & 1) * 16;
+  return cat44(ld_tr4_s<128>(tile, r, c, lane & 15), ld_tr4_s<128>(tile, r + 8, c, lane & 15));
+}
+template <> __device__ inline bf16x8 ld_frag_kcrow_s<bf16, 64>(const bf16* tile, int row0, int ci, int lane, int col0) {
+  const int r = row0 + 16 * ci + 4 * (lane >> 5), c = col0 + ((lane >> 4) & 1) * 16;
+  return cat44(ld_tr4_s<64>(tile, r, c, lane & 15), ld_tr4_s<64>(tile, r + 8, c, lane & 15));
+}
+template <> __device__ inline float ld_frag_kcrow_s<float, 128>(const float* tile, int row0, int ci, int lane, int col0) {
+  return tile[Swz<float, 128>::idx(row0 + c_row(ci, lane >> 5), col0 + (lane & 31))];
+}
+template <> __device__ inline float ld_frag_kcrow_s<float, 64>(const float* tile, int row0, int ci, int lane, int col0) {
+  return tile[Swz<float, 64>::idx(row0 + c_row(ci, lane >> 5), col0 + (lane & 31))];
+}
+
+// Global -> LDS DMA of rows [k0, k0+NR) of a [rows, heads, D] array (row
+// stride rs elements, pointer at the head) into a swizzled tile.  Wave `wave`
+// of `nw` issues every nw-th 1 KB block; each lane moves one 16-byte chunk.
+// Rows at or past kmax re-read row kmax-1 (finite data; callers mask them).
+template <typename T, int NR, int D>
+__device__ inline void dma_rows(T* tile, const T* base, int64_t rs, int k0, int kmax, int wave, int nw, int lane) {
+  using S = Swz<T, D>;
+  constexpr int NBLK = NR / S::RPB;
+  static_assert(NR % S::RPB == 0, "tile rows must fill whole DMA blocks");
+  const int lr = lane / S::CH, pc = lane % S::CH;
+  for (int bb = wave; bb < NBLK; bb += nw) {
+    const int r = bb * S::RPB + lr;
+    const int c = pc ^ (r & (S::CH - 1));
+    int k = k0 + r;
+    if (k >= kmax) k = kmax - 1;
+    const T* src = base + (int64_t)k * rs + c * S::EPC;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(tile + bb * S::RPB * D), 16, 0, 0);
+  }
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// global->LDS DMA) have completed: s_waitcnt vmcnt(0).
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Pack C-layout values acc[ci*KPL .. ci*KPL+KPL) into an MFMA fragment.
 template <typename T> __device__ inline typename Elt<T>::Frag pack_frag(const float* v);
 template <> __device__ inline bf16x8 pack_frag<bf16>(const float* v) {

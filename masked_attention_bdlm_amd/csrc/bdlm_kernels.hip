@@ -104,16 +104,15 @@ __device__ inline void stage_rows_dual(T* lds_r, T* lds_t, const T* base, int64_
 
 // ================================================================= forward
 template <typename T, int D, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs args) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArgs args) {
   using E = Elt<T>;
   using Frag = typename E::Frag;
   constexpr int M = 128, N = 64;
   constexpr int KPL = E::KPL, KC = 2 * KPL;
   constexpr int DCH = D / KC;          // k-chunks over head_dim
   constexpr int CPS = 32 / KC;         // k-chunks per 32-key subtile
-  constexpr int KST = D + E::PAD;      // K / V tile row stride
-  __shared__ __attribute__((aligned(16))) T k_lds[N * KST];
-  __shared__ __attribute__((aligned(16))) T v_lds[N * KST];
+  // K and V tiles, double-buffered, filled by global->LDS DMA (swizzled rows)
+  __shared__ __attribute__((aligned(16))) T kv_lds[2][2][N * D];
 
   const Problem& p = args.p;
   int bg, item;
@@ -146,10 +145,27 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs args) {
     }
   }
 
-  int lo[2], hi[2];
+  // key tiles: array 0 (clean) then array 1 (corrupted / local)
+  int klo[2], khi[2], flo[2], fhi[2], nt[2], lo[2], hi[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    tile_ranges(p, s, a, r0, r1, klo[a], khi[a], flo[a], fhi[a]);
+    nt[a] = klo[a] < khi[a] ? (khi[a] - klo[a] + N - 1) / N : 0;
     if (valid) row_keys(p, s, r, a, lo[a], hi[a]); else lo[a] = hi[a] = 0;
+  }
+  const int total = nt[0] + nt[1];
+  const int64_t rs = (int64_t)p.hkv * D;
+  const T* kb[2];
+  const T* vb[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    kb[a] = reinterpret_cast<const T*>(args.k[a]) + (int64_t)b * p.klen[a] * rs + (int64_t)g * D;
+    vb[a] = reinterpret_cast<const T*>(args.v[a]) + (int64_t)b * p.klen[a] * rs + (int64_t)g * D;
+  }
+  if (total > 0) {
+    const int a0 = nt[0] > 0 ? 0 : 1;
+    dma_rows<T, N, D>(kv_lds[0][0], kb[a0], rs, klo[a0], khi[a0], w, 4, lane);
+    dma_rows<T, N, D>(kv_lds[0][1], vb[a0], rs, klo[a0], khi[a0], w, 4, lane);
   }
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -157,78 +173,103 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs args) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
 
-  for (int a = 0; a < 2; ++a) {
-    int klo, khi, flo, fhi;
-    tile_ranges(p, s, a, r0, r1, klo, khi, flo, fhi);
-    if (klo >= khi) continue;
-    const int64_t rs = (int64_t)p.hkv * D;
-    const T* kbase = reinterpret_cast<const T*>(args.k[a]) + (int64_t)b * p.klen[a] * rs + (int64_t)g * D;
-    const T* vbase = reinterpret_cast<const T*>(args.v[a]) + (int64_t)b * p.klen[a] * rs + (int64_t)g * D;
-    const int mylo = lo[a], myhi = hi[a];
+  for (int it = 0; it < total; ++it) {
+    const int a = it < nt[0] ? 0 : 1;
+    const int k0 = klo[a] + (it - (a ? nt[0] : 0)) * N;
+    wait_vmem();
+    __syncthreads();   // tile `it` is in buffer it&1; buffer (it+1)&1 is free
+    if (it + 1 < total) {
+      const int a2 = it + 1 < nt[0] ? 0 : 1;
+      const int k02 = klo[a2] + (it + 1 - (a2 ? nt[0] : 0)) * N;
+      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][0], kb[a2], rs, k02, khi[a2], w, 4, lane);
+      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, 4, lane);
+    }
+    const T* k_lds = kv_lds[it & 1][0];
+    const T* v_lds = kv_lds[it & 1][1];
+    const bool need_mask = !(k0 >= flo[a] && k0 + N <= fhi[a]);
+    const int mylo = a ? lo[1] : lo[0], myhi = a ? hi[1] : hi[0];
 
-    for (int k0 = klo; k0 < khi; k0 += N) {
-      __syncthreads();
-      stage_rows<T, N, D, KST>(k_lds, kbase, rs, k0, khi, tid);
-      stage_rows<T, N, D, KST>(v_lds, vbase, rs, k0, khi, tid);
-      __syncthreads();
-      const bool need_mask = !(k0 >= flo && k0 + N <= fhi);
-
-      // S^T[key][query] for the N keys of the tile.
-      f32x16 sacc[N / 32];
+    // S^T[key][query] for the N keys of the tile; K fragments are read in
+    // batches of 4 k-chunks one batch ahead of the MFMAs that use them.
+    f32x16 sacc[N / 32];
+    {
+      constexpr int BT = DCH < 4 ? DCH : 4;
+      constexpr int NB = (N / 32) * (DCH / BT);       // batches over (sub, chunk)
+      Frag ka[2][BT];
 #pragma unroll
-      for (int sub = 0; sub < N / 32; ++sub) {
-        sacc[sub] = f32x16{};
+      for (int c = 0; c < BT; ++c) ka[0][c] = ld_frag_s<T, D>(k_lds, ln, c * KC + hh * KPL);
 #pragma unroll
-        for (int c = 0; c < DCH; ++c) {
-          Frag ka = ld_frag<T>(k_lds + (sub * 32 + ln) * KST + c * KC + hh * KPL);
-          sacc[sub] = E::mma(ka, qf[c], sacc[sub]);
+      for (int sub = 0; sub < N / 32; ++sub) sacc[sub] = f32x16{};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (nb + 1 < NB) {
+          const int sub2 = (nb + 1) / (DCH / BT), cb2 = (nb + 1) % (DCH / BT);
+#pragma unroll
+          for (int c = 0; c < BT; ++c)
+            ka[(nb + 1) & 1][c] = ld_frag_s<T, D>(k_lds, sub2 * 32 + ln, (cb2 * BT + c) * KC + hh * KPL);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        const int sub = nb / (DCH / BT), cb = nb % (DCH / BT);
+#pragma unroll
+        for (int c = 0; c < BT; ++c) sacc[sub] = E::mma(ka[nb & 1][c], qf[cb * BT + c], sacc[sub]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
 
-      float mx = -INFINITY;
+    float mx = -INFINITY;
 #pragma unroll
-      for (int sub = 0; sub < N / 32; ++sub) {
+    for (int sub = 0; sub < N / 32; ++sub) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float v = sacc[sub][i];
-          if (need_mask) {
-            const int kk = k0 + sub * 32 + c_row(i, hh);
-            if (kk < mylo || kk >= myhi) v = -INFINITY;
-          }
-          sacc[sub][i] = v;
-          mx = fmaxf(mx, v);
+      for (int i = 0; i < 16; ++i) {
+        float v = sacc[sub][i];
+        if (need_mask) {
+          const int kk = k0 + sub * 32 + c_row(i, hh);
+          if (kk < mylo || kk >= myhi) v = -INFINITY;
         }
+        sacc[sub][i] = v;
+        mx = fmaxf(mx, v);
       }
-      mx = fmaxf(mx, wave_swap32(mx));
-      const float m_new = fmaxf(m_run, mx * args.scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-      l_run *= alpha;
+    }
+    mx = fmaxf(mx, wave_swap32(mx));
+    const float m_new = fmaxf(m_run, mx * args.scale_log2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
 
-      float pv[N / 32][16];
+    float pv[N / 32][16];
 #pragma unroll
-      for (int sub = 0; sub < N / 32; ++sub) {
+    for (int sub = 0; sub < N / 32; ++sub) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(sacc[sub][i] * args.scale_log2 - m_use);
-          pv[sub][i] = e;
-          l_run += e;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(sacc[sub][i] * args.scale_log2 - m_use);
+        pv[sub][i] = e;
+        l_run += e;
       }
+    }
 
-      // O^T[d][query] += V^T[d][key] P^T[key][query]
+    // O^T[d][query] += V^T[d][key] P^T[key][query]; the V^T fragments of one
+    // d-tile are read while the previous d-tile's MFMAs run
+    Frag pb[N / KC];
+#pragma unroll
+    for (int cc = 0; cc < N / KC; ++cc) pb[cc] = pack_frag<T>(&pv[cc / CPS][(cc % CPS) * KPL]);
+    {
+      Frag va[2][N / KC];
+#pragma unroll
+      for (int cc = 0; cc < N / KC; ++cc) va[0][cc] = ld_frag_kcrow_s<T, D>(v_lds, (cc / CPS) * 32, cc % CPS, lane, 0);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
+        if (dt + 1 < D / 32) {
 #pragma unroll
-        for (int cc = 0; cc < N / KC; ++cc) {
-          const int sub = cc / CPS, ci = cc % CPS;
-          Frag va = ld_frag_kcrow<T>(v_lds, KST, sub * 32, ci, lane, dt * 32);
-          Frag pb = pack_frag<T>(&pv[sub][ci * KPL]);
-          oacc[dt] = E::mma(va, pb, oacc[dt]);
+          for (int cc = 0; cc < N / KC; ++cc)
+            va[(dt + 1) & 1][cc] = ld_frag_kcrow_s<T, D>(v_lds, (cc / CPS) * 32, cc % CPS, lane, (dt + 1) * 32);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cc = 0; cc < N / KC; ++cc) oacc[dt] = E::mma(va[dt & 1][cc], pb[cc], oacc[dt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -625,9 +666,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
   constexpr int KPL = E::KPL, KC = 2 * KPL;
   constexpr int DCH = D / KC;
   constexpr int CPS = 32 / KC;
-  constexpr int KST = D + E::PAD;
-  __shared__ __attribute__((aligned(16))) T k_lds[N * KST];
-  __shared__ __attribute__((aligned(16))) T v_lds[N * KST];
+  // K and V tiles, double-buffered, filled by global->LDS DMA (swizzled rows)
+  __shared__ __attribute__((aligned(16))) T kv_lds[2][2][N * D];
 
   const Problem& p = args.p;
   int bg, item;
@@ -668,105 +708,118 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
     lse2 = args.lse[s][ri] * kLog2e;
     dd = args.delta[s][ri];
   }
-  int lo[2], hi[2];
+  int klo[2], khi[2], flo[2], fhi[2], nt[2], lo[2], hi[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    tile_ranges(p, s, a, r0, r1, klo[a], khi[a], flo[a], fhi[a]);
+    nt[a] = klo[a] < khi[a] ? (khi[a] - klo[a] + N - 1) / N : 0;
     if (valid) row_keys(p, s, r, a, lo[a], hi[a]); else lo[a] = hi[a] = 0;
+  }
+  const int total = nt[0] + nt[1];
+  const int64_t rs = (int64_t)p.hkv * D;
+  const T* kb[2];
+  const T* vb[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    kb[a] = reinterpret_cast<const T*>(args.k[a]) + (int64_t)b * p.klen[a] * rs + (int64_t)g * D;
+    vb[a] = reinterpret_cast<const T*>(args.v[a]) + (int64_t)b * p.klen[a] * rs + (int64_t)g * D;
+  }
+  if (total > 0) {
+    const int a0 = nt[0] > 0 ? 0 : 1;
+    dma_rows<T, N, D>(kv_lds[0][0], kb[a0], rs, klo[a0], khi[a0], w, 4, lane);
+    dma_rows<T, N, D>(kv_lds[0][1], vb[a0], rs, klo[a0], khi[a0], w, 4, lane);
   }
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  bool any = false;
 
-  for (int a = 0; a < 2; ++a) {
-    int klo, khi, flo, fhi;
-    tile_ranges(p, s, a, r0, r1, klo, khi, flo, fhi);
-    if (klo >= khi) continue;
-    any = true;
-    const int64_t rs = (int64_t)p.hkv * D;
-    const T* kbase = reinterpret_cast<const T*>(args.k[a]) + (int64_t)b * p.klen[a] * rs + (int64_t)g * D;
-    const T* vbase = reinterpret_cast<const T*>(args.v[a]) + (int64_t)b * p.klen[a] * rs + (int64_t)g * D;
-    const int mylo = lo[a], myhi = hi[a];
+  for (int it = 0; it < total; ++it) {
+    const int a = it < nt[0] ? 0 : 1;
+    const int k0 = klo[a] + (it - (a ? nt[0] : 0)) * N;
+    wait_vmem();
+    __syncthreads();   // tile `it` is in buffer it&1; buffer (it+1)&1 is free
+    if (it + 1 < total) {
+      const int a2 = it + 1 < nt[0] ? 0 : 1;
+      const int k02 = klo[a2] + (it + 1 - (a2 ? nt[0] : 0)) * N;
+      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][0], kb[a2], rs, k02, khi[a2], w, 4, lane);
+      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, 4, lane);
+    }
+    const T* k_lds = kv_lds[it & 1][0];
+    const T* v_lds = kv_lds[it & 1][1];
+    const bool need_mask = !(k0 >= flo[a] && k0 + N <= fhi[a]) || (r1 - r0 < M);
+    const int mylo = a ? lo[1] : lo[0], myhi = a ? hi[1] : hi[0];
 
-    for (int k0 = klo; k0 < khi; k0 += N) {
-      __syncthreads();
-      stage_rows<T, N, D, KST>(k_lds, kbase, rs, k0, khi, tid);
-      stage_rows<T, N, D, KST>(v_lds, vbase, rs, k0, khi, tid);
-      __syncthreads();
-      const bool need_mask = !(k0 >= flo && k0 + N <= fhi) || (r1 - r0 < M);
-
-      // per 32-key sub-tile: S^T = K Q^T and dP^T = V dO^T, then
-      // dS^T = P^T (dP^T - D) with P^T = exp(S^T - LSE), then dQ^T += K^T dS^T
+    // per 32-key sub-tile: S^T = K Q^T and dP^T = V dO^T, then
+    // dS^T = P^T (dP^T - D) with P^T = exp(S^T - LSE), then dQ^T += K^T dS^T
 #pragma unroll
-      for (int sub = 0; sub < N / 32; ++sub) {
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
-        {
-          constexpr int BT = DCH < 4 ? DCH : 4;
-          Frag ka[2][BT], va[2][BT];
+    for (int sub = 0; sub < N / 32; ++sub) {
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      {
+        constexpr int BT = DCH < 4 ? DCH : 4;
+        Frag ka[2][BT], va[2][BT];
 #pragma unroll
-          for (int c = 0; c < BT; ++c) {
-            ka[0][c] = ld_frag<T>(k_lds + (sub * 32 + ln) * KST + c * KC + hh * KPL);
-            va[0][c] = ld_frag<T>(v_lds + (sub * 32 + ln) * KST + c * KC + hh * KPL);
-          }
+        for (int c = 0; c < BT; ++c) {
+          ka[0][c] = ld_frag_s<T, D>(k_lds, sub * 32 + ln, c * KC + hh * KPL);
+          va[0][c] = ld_frag_s<T, D>(v_lds, sub * 32 + ln, c * KC + hh * KPL);
+        }
 #pragma unroll
-          for (int cb = 0; cb < DCH / BT; ++cb) {
-            if (cb + 1 < DCH / BT) {
-#pragma unroll
-              for (int c = 0; c < BT; ++c) {
-                const int cc = (cb + 1) * BT + c;
-                ka[(cb + 1) & 1][c] = ld_frag<T>(k_lds + (sub * 32 + ln) * KST + cc * KC + hh * KPL);
-                va[(cb + 1) & 1][c] = ld_frag<T>(v_lds + (sub * 32 + ln) * KST + cc * KC + hh * KPL);
-              }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int cb = 0; cb < DCH / BT; ++cb) {
+          if (cb + 1 < DCH / BT) {
 #pragma unroll
             for (int c = 0; c < BT; ++c) {
-              sacc = E::mma(ka[cb & 1][c], qf[cb * BT + c], sacc);
-              pacc = E::mma(va[cb & 1][c], df[cb * BT + c], pacc);
+              const int cc = (cb + 1) * BT + c;
+              ka[(cb + 1) & 1][c] = ld_frag_s<T, D>(k_lds, sub * 32 + ln, cc * KC + hh * KPL);
+              va[(cb + 1) & 1][c] = ld_frag_s<T, D>(v_lds, sub * 32 + ln, cc * KC + hh * KPL);
             }
-            __builtin_amdgcn_sched_barrier(0);
           }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < BT; ++c) {
+            sacc = E::mma(ka[cb & 1][c], qf[cb * BT + c], sacc);
+            pacc = E::mma(va[cb & 1][c], df[cb * BT + c], pacc);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        Frag dsf[CPS];
+      }
+      Frag dsf[CPS];
 #pragma unroll
-        for (int ci = 0; ci < CPS; ++ci) {
-          float de[KPL];
+      for (int ci = 0; ci < CPS; ++ci) {
+        float de[KPL];
 #pragma unroll
-          for (int jj = 0; jj < KPL; ++jj) {
-            const int i = ci * KPL + jj;
-            float e = fast_exp2(sacc[i] * args.scale_log2 - lse2);
-            if (need_mask) {
-              const int kk = k0 + sub * 32 + c_row(i, hh);
-              if (kk < mylo || kk >= myhi) e = 0.f;
-            }
-            de[jj] = e * (pacc[i] - dd);
+        for (int jj = 0; jj < KPL; ++jj) {
+          const int i = ci * KPL + jj;
+          float e = fast_exp2(sacc[i] * args.scale_log2 - lse2);
+          if (need_mask) {
+            const int kk = k0 + sub * 32 + c_row(i, hh);
+            if (kk < mylo || kk >= myhi) e = 0.f;
           }
-          dsf[ci] = pack_frag<T>(de);
+          de[jj] = e * (pacc[i] - dd);
         }
-        // dQ^T[d][query] += K^T[d][key] dS^T[key][query]
-        {
-          Frag kt[2][CPS];
+        dsf[ci] = pack_frag<T>(de);
+      }
+      // dQ^T[d][query] += K^T[d][key] dS^T[key][query]
+      {
+        Frag kt[2][CPS];
 #pragma unroll
-          for (int ci = 0; ci < CPS; ++ci) kt[0][ci] = ld_frag_kcrow<T>(k_lds, KST, sub * 32, ci, lane, 0);
+        for (int ci = 0; ci < CPS; ++ci) kt[0][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, 0);
 #pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            if (dt + 1 < D / 32) {
+        for (int dt = 0; dt < D / 32; ++dt) {
+          if (dt + 1 < D / 32) {
 #pragma unroll
-              for (int ci = 0; ci < CPS; ++ci)
-                kt[(dt + 1) & 1][ci] = ld_frag_kcrow<T>(k_lds, KST, sub * 32, ci, lane, (dt + 1) * 32);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ci = 0; ci < CPS; ++ci) acc[dt] = E::mma(kt[dt & 1][ci], dsf[ci], acc[dt]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int ci = 0; ci < CPS; ++ci)
+              kt[(dt + 1) & 1][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, (dt + 1) * 32);
           }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ci = 0; ci < CPS; ++ci) acc[dt] = E::mma(kt[dt & 1][ci], dsf[ci], acc[dt]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   }
 
-  if (valid && any) {
+  if (valid && (total > 0 || !ADD_F32)) {
     using OT = typename std::conditional<ADD_F32, float, T>::type;
     OT* orow = reinterpret_cast<OT*>(args.dq[s]) + ((int64_t)b * R + r) * qrs + (int64_t)h * D;
 #pragma unroll
@@ -782,11 +835,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
         }
       }
     }
-  } else if (valid && !ADD_F32) {
-    // a row that sees no key in full mode cannot exist; keep the output defined
-    using OT = typename std::conditional<ADD_F32, float, T>::type;
-    OT* orow = reinterpret_cast<OT*>(args.dq[s]) + ((int64_t)b * R + r) * qrs + (int64_t)h * D;
-    for (int d = hh; d < D; d += 2) orow[d] = static_cast<OT>(0.f);
   }
 }
 
