@@ -333,25 +333,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs args) {
   (void)s;
 }
 
-// ======================================================= backward: main kernel
-// Per-thread register copy of one Q/dO tile slice (RPT rows x VEC columns)
-// plus the row data of row `tid` (threads < M), loaded one iteration ahead.
-template <typename T, int M, int D>
-struct BwdPrefetch {
-  static constexpr int VEC = Elt<T>::VEC;
-  static constexpr int RPT = M * D / (256 * VEC);
-  Vec16 q[RPT], d[RPT];
-  float lse2, delta;
-  int lo, hi;
-};
-
-// Iteration order of a backward workgroup: query tiles descending; at each
-// tile position the (up to two) query streams that see the key tile, then the
-// q heads of the GQA group.  Workgroups of one kv head therefore sweep the
-// same query tiles at the same time.
-// Iteration order of a backward workgroup: query tiles descending; at each
-// tile position the (up to two) query streams that see the key tile, then the
-// q heads of the GQA group.  Workgroups of one kv head therefore sweep the
+// ==================================================== backward: dK/dV kernel
+// Iteration order of a key-major backward workgroup: query tiles descending; at
+// each tile position the (up to two) query streams that see the key tile, then
+// the q heads of the GQA group.  Workgroups of one kv head therefore sweep the
 // same query tiles at the same time.  The order is a handful of uniform
 // integers: o[0..11] = s0, s1, tlo0, thi0, tlo1, thi1, inter, tb, slow,
 // nboth, n0, total.
@@ -404,60 +389,14 @@ __device__ __forceinline__ void bwd_order(const Problem& p, int a, int ns0, int 
     h = g * G + hg_;                                               \
   } while (0)
 
-// Global -> registers: this thread's RPT x VEC slice of the Q and dO tiles of
-// (stream s, rows q0.., head h), and the row data of row `tid` (threads < M).
-template <typename T, int M, int D>
-__device__ __forceinline__ void bwd_load(const BwdArgs& args, int s, int q0, int h, int a, int b, int tid,
-                                         BwdPrefetch<T, M, D>& pf) {
-  using PF = BwdPrefetch<T, M, D>;
-  constexpr int RPT = PF::RPT, VEC = PF::VEC, RG = M / RPT;
-  const Problem& p = args.p;
-  const int R = p.rows[s];
-  const int q1 = min(q0 + M, R);
-  const int64_t qrs = (int64_t)p.hq * D;
-  const int rg = tid % RG, dcol = (tid / RG) * VEC;
-  const T* qb = reinterpret_cast<const T*>(args.q[s]) + (int64_t)b * R * qrs + (int64_t)h * D + dcol;
-  const T* db = reinterpret_cast<const T*>(args.dout[s]) + (int64_t)b * R * qrs + (int64_t)h * D + dcol;
-#pragma unroll
-  for (int jj = 0; jj < RPT; ++jj) {
-    const int r = q0 + rg * RPT + jj;
-    pf.q[jj] = r < q1 ? ld16(qb + (int64_t)r * qrs) : zero16();
-    pf.d[jj] = r < q1 ? ld16(db + (int64_t)r * qrs) : zero16();
-  }
-  if (tid < M) {
-    const int rr = q0 + tid;
-    int lo = 0, hi = 0;
-    float l2 = 0.f, dd = 0.f;
-    if (rr < q1) {
-      row_keys(p, s, rr, a, lo, hi);
-      const int64_t ri = ((int64_t)b * p.hq + h) * R + rr;
-      l2 = args.lse[s][ri] * kLog2e;
-      dd = args.delta[s][ri];
-    }
-    pf.lo = lo; pf.hi = hi; pf.lse2 = l2; pf.delta = dd;
-  }
-}
-
-// Registers -> LDS: the Q/dO slice (row-major) and the row data.
-template <typename T, int M, int D, int QST>
-__device__ __forceinline__ void bwd_store(T* q_l, T* do_l, float* lse_l, float* dl_l, int* lo_l, int* hi_l, int tid,
-                                          const BwdPrefetch<T, M, D>& pf) {
-  using PF = BwdPrefetch<T, M, D>;
-  constexpr int RPT = PF::RPT, VEC = PF::VEC, RG = M / RPT;
-  const int rg = tid % RG, dcol = (tid / RG) * VEC;
-#pragma unroll
-  for (int jj = 0; jj < RPT; ++jj) {
-    st16(q_l + (rg * RPT + jj) * QST + dcol, pf.q[jj]);
-    st16(do_l + (rg * RPT + jj) * QST + dcol, pf.d[jj]);
-  }
-  if (tid < M) {
-    lse_l[tid] = pf.lse2;
-    dl_l[tid] = pf.delta;
-    lo_l[tid] = pf.lo;
-    hi_l[tid] = pf.hi;
-  }
-}
-
+// Key-major dK/dV: one workgroup per (batch, kv-head, key array, 128-key
+// tile); wave w owns 32 keys and keeps K_w, V_w (MFMA B operands) and its dK_w,
+// dV_w accumulators in registers while it sweeps the visible 64-row query
+// tiles of every q head of the GQA group.  S = Q K_w^T and dP = dO V_w^T put
+// the key on the lane, so P and dS are directly the A operands of
+// dV += P^T dO and dK += dS^T Q; their dO / Q operands are read transposed out
+// of the row-major tiles.  Q/dO tiles and the per-row LSE / D are
+// double-buffered in LDS and filled by global->LDS DMA one iteration ahead.
 template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
   using E = Elt<T>;
@@ -468,17 +407,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
   constexpr int KPL = E::KPL, KC = 2 * KPL;
   constexpr int DCH = D / KC;
   constexpr int CPS = 32 / KC;
-  constexpr int VEC = E::VEC;
-  constexpr int QST = D + E::PAD;      // q / dO / K row stride
-  using PF = BwdPrefetch<T, M, D>;
-  constexpr int RPT = PF::RPT;
-  static_assert(RPT >= 1 && M * D == 256 * VEC * RPT, "tile/thread mismatch");
-  constexpr int RG = M / RPT;
-  __shared__ __attribute__((aligned(16))) T q_lds[2][M * QST];
-  __shared__ __attribute__((aligned(16))) T do_lds[2][M * QST];
-  __shared__ __attribute__((aligned(16))) float lse_l[2][M];
-  __shared__ __attribute__((aligned(16))) float dl_l[2][M];
-  __shared__ int lo_l[2][M], hi_l[2][M];
+  __shared__ __attribute__((aligned(16))) T qd_lds[2][2][M * D];     // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float row_l[2][2][64];      // [buffer][LSE, D]
+  __shared__ int lh_l[2][2][M];                                       // [buffer][lo, hi]
 
   const Problem& p = args.p;
   int bg, item;
@@ -506,29 +437,46 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
     vf[c] = ld_frag<T>(vbase + off);
     if (!kvalid) { kf[c] = Frag{}; vf[c] = Frag{}; }
   }
+
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) { dkacc[dt] = f32x16{}; dvacc[dt] = f32x16{}; }
 
-  // ---- iteration space: q tiles descending; at each tile position the
-  // streams that see this key tile, then the heads of the GQA group.  All
-  // workgroups of a kv head sweep the same query tiles at the same time.
   int o[12];
   bwd_order(p, a, args.ns0, k0, k1, M, o);
   const int o_s0 = o[0], o_s1 = o[1], o_thi0 = o[3], o_thi1 = o[5], o_inter = o[6], o_tb = o[7];
   const int o_slow = o[8], o_nboth = o[9], o_n0 = o[10], total = o[11];
   const int G = p.group;
-  // One barrier per iteration: after it, tiles of `it` are in buffer `cur`
-  // and every wave has finished reading buffer cur^1; the loads of the next
-  // tiles are issued into registers, the main block runs, and the next tiles
-  // are written into buffer cur^1 at the end.
-  PF pf;
-  if (total > 0) {
-    int s_, q0_, h_;
-    BWD_DECODE(0, s_, q0_, h_);
-    bwd_load<T, M, D>(args, s_, q0_, h_, a, b, tid, pf);
-    bwd_store<T, M, D, QST>(q_lds[0], do_lds[0], lse_l[0], dl_l[0], lo_l[0], hi_l[0], tid, pf);
-  }
+  const int64_t qrs = (int64_t)p.hq * D;
+
+  // DMA of iteration `it`'s Q/dO tiles and row data into buffer `buf`; rows past
+  // the stream end re-read its last row and are masked in the main block.
+#define DKDV_ISSUE(it, buf)                                                                      \
+  do {                                                                                           \
+    int s_, q0_, h_;                                                                             \
+    BWD_DECODE(it, s_, q0_, h_);                                                                 \
+    const int R_ = p.rows[s_];                                                                   \
+    const int q1_ = min(q0_ + M, R_);                                                            \
+    const int64_t hb_ = (int64_t)b * R_ * qrs + (int64_t)h_ * D;                                 \
+    dma_rows<T, M, D>(qd_lds[buf][0], reinterpret_cast<const T*>(args.q[s_]) + hb_, qrs, q0_, q1_, \
+                      w, 4, lane);                                                               \
+    dma_rows<T, M, D>(qd_lds[buf][1], reinterpret_cast<const T*>(args.dout[s_]) + hb_, qrs, q0_,   \
+                      q1_, w, 4, lane);                                                          \
+    if (w < 2) {                                                                                 \
+      const int64_t ri_ = ((int64_t)b * p.hq + h_) * R_ + min(q0_ + lane, q1_ - 1);              \
+      const float* src_ = (w == 0 ? args.lse[s_] : args.delta[s_]) + ri_;                        \
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src_,      \
+                                       (__attribute__((address_space(3))) void*)(row_l[buf][w]), 4, 0, 0); \
+    }                                                                                            \
+    if (tid < M) {                                                                               \
+      int lo_ = 0, hi_ = 0;                                                                      \
+      if (q0_ + tid < q1_) row_keys(p, s_, q0_ + tid, a, lo_, hi_);                              \
+      lh_l[buf][0][tid] = lo_;                                                                   \
+      lh_l[buf][1][tid] = hi_;                                                                   \
+    }                                                                                            \
+  } while (0)
+
+  if (total > 0) DKDV_ISSUE(0, 0);
   const float sl2 = args.scale_log2;
   for (int it = 0; it < total; ++it) {
     const int cur = it & 1;
@@ -538,30 +486,28 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
     const int q1 = min(q0 + M, R);
     int klo, khi, flo, fhi;
     tile_ranges(p, s, a, q0, q1, klo, khi, flo, fhi);
-    const bool need_mask = !(k0 >= flo && k0 + N <= fhi);
-    __syncthreads();
-    if (it + 1 < total) {
-      int s2, q02, h2;
-      BWD_DECODE(it + 1, s2, q02, h2);
-      bwd_load<T, M, D>(args, s2, q02, h2, a, b, tid, pf);
-    }
-    const T* qt = q_lds[cur];
-    const T* dot = do_lds[cur];
+    const bool need_mask = !(k0 >= flo && k0 + N <= fhi) || (q1 - q0 < M);
+    wait_vmem();
+    __syncthreads();   // buffer `cur` holds iteration it; buffer cur^1 is free
+    if (it + 1 < total) DKDV_ISSUE(it + 1, cur ^ 1);
+    const T* qt = qd_lds[cur][0];
+    const T* dot = qd_lds[cur][1];
+    const float* lse_r = row_l[cur][0];
+    const float* dl_r = row_l[cur][1];
+
     // One 32-row query sub-tile at a time: S = Q K_w^T and dP = dO V_w^T
     // (rows = queries, column = this lane's key), then P and dS, then their
-    // contributions to dV_w and dK_w, then dS^T into LDS.
+    // contributions to dV_w and dK_w.
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       {
-        // operand fragments are read in batches of 4 k-chunks, one batch ahead
-        // of the MFMAs that consume them
         constexpr int BT = DCH < 4 ? DCH : 4;
         Frag qa[2][BT], da[2][BT];
 #pragma unroll
         for (int c = 0; c < BT; ++c) {
-          qa[0][c] = ld_frag<T>(qt + (qs * 32 + ln) * QST + c * KC + hh * KPL);
-          da[0][c] = ld_frag<T>(dot + (qs * 32 + ln) * QST + c * KC + hh * KPL);
+          qa[0][c] = ld_frag_s<T, D>(qt, qs * 32 + ln, c * KC + hh * KPL);
+          da[0][c] = ld_frag_s<T, D>(dot, qs * 32 + ln, c * KC + hh * KPL);
         }
 #pragma unroll
         for (int cb = 0; cb < DCH / BT; ++cb) {
@@ -569,8 +515,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
 #pragma unroll
             for (int c = 0; c < BT; ++c) {
               const int cc = (cb + 1) * BT + c;
-              qa[(cb + 1) & 1][c] = ld_frag<T>(qt + (qs * 32 + ln) * QST + cc * KC + hh * KPL);
-              da[(cb + 1) & 1][c] = ld_frag<T>(dot + (qs * 32 + ln) * QST + cc * KC + hh * KPL);
+              qa[(cb + 1) & 1][c] = ld_frag_s<T, D>(qt, qs * 32 + ln, cc * KC + hh * KPL);
+              da[(cb + 1) & 1][c] = ld_frag_s<T, D>(dot, qs * 32 + ln, cc * KC + hh * KPL);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -584,39 +530,57 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
       }
       // P = exp(S - LSE), dS = P (dP - D); masked pairs get P = 0.  Both are
       // packed into MFMA fragments right away (k = queries in C-row order).
+      float pe[16], de[16];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int rr0 = qs * 32 + c_row(4 * i4, hh);      // 4 consecutive rows
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_r + rr0);
+        const float4 d4 = *reinterpret_cast<const float4*>(dl_r + rr0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int i = 4 * i4 + jj;
+          const float e = fast_exp2(sacc[i] * sl2 - lv[jj] * kLog2e);
+          pe[i] = e;
+          de[i] = dv[jj];
+        }
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int rr = qs * 32 + c_row(i, hh);
+          if (!(kk >= lh_l[cur][0][rr] && kk < lh_l[cur][1][rr])) pe[i] = 0.f;
+        }
+      }
       Frag pfr[CPS], sfr[CPS];
 #pragma unroll
       for (int ci = 0; ci < CPS; ++ci) {
-        float pe[KPL], de[KPL];
+        float d8[KPL];
 #pragma unroll
         for (int jj = 0; jj < KPL; ++jj) {
           const int i = ci * KPL + jj;
-          const int rr = qs * 32 + c_row(i, hh);
-          float e = fast_exp2(sacc[i] * sl2 - lse_l[cur][rr]);
-          if (need_mask && !(kk >= lo_l[cur][rr] && kk < hi_l[cur][rr])) e = 0.f;
-          pe[jj] = e;
-          de[jj] = e * (pacc[i] - dl_l[cur][rr]);
+          d8[jj] = pe[i] * (pacc[i] - de[i]);
         }
-        pfr[ci] = pack_frag<T>(pe);
-        sfr[ci] = pack_frag<T>(de);
+        pfr[ci] = pack_frag<T>(&pe[ci * KPL]);
+        sfr[ci] = pack_frag<T>(d8);
       }
       // dV_w += P^T dO ; dK_w += dS^T Q  (the dO / Q fragments are read
       // transposed out of the row-major tiles)
       {
-        // fragments of one d-tile are read while the previous d-tile's MFMAs run
         Frag ob[2][CPS], qb2[2][CPS];
 #pragma unroll
         for (int ci = 0; ci < CPS; ++ci) {
-          ob[0][ci] = ld_frag_kcrow<T>(dot, QST, qs * 32, ci, lane, 0);
-          qb2[0][ci] = ld_frag_kcrow<T>(qt, QST, qs * 32, ci, lane, 0);
+          ob[0][ci] = ld_frag_kcrow_s<T, D>(dot, qs * 32, ci, lane, 0);
+          qb2[0][ci] = ld_frag_kcrow_s<T, D>(qt, qs * 32, ci, lane, 0);
         }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           if (dt + 1 < D / 32) {
 #pragma unroll
             for (int ci = 0; ci < CPS; ++ci) {
-              ob[(dt + 1) & 1][ci] = ld_frag_kcrow<T>(dot, QST, qs * 32, ci, lane, (dt + 1) * 32);
-              qb2[(dt + 1) & 1][ci] = ld_frag_kcrow<T>(qt, QST, qs * 32, ci, lane, (dt + 1) * 32);
+              ob[(dt + 1) & 1][ci] = ld_frag_kcrow_s<T, D>(dot, qs * 32, ci, lane, (dt + 1) * 32);
+              qb2[(dt + 1) & 1][ci] = ld_frag_kcrow_s<T, D>(qt, qs * 32, ci, lane, (dt + 1) * 32);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -629,10 +593,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
         }
       }
     }
-    if (it + 1 < total)
-      bwd_store<T, M, D, QST>(q_lds[cur ^ 1], do_lds[cur ^ 1], lse_l[cur ^ 1], dl_l[cur ^ 1], lo_l[cur ^ 1],
-                              hi_l[cur ^ 1], tid, pf);
   }
+#undef DKDV_ISSUE
 
   // dK = scale * sum dS^T Q, dV = sum P^T dO for the wave's 32 keys.
   T* dkb = reinterpret_cast<T*>(args.dk[a]) + (int64_t)b * p.klen[a] * krs + (int64_t)g * D;
