@@ -145,26 +145,32 @@ def main():
 
     P = visible_pairs(w.seqlen, w.block)
     heads = w.batch * w.hq
-    flop_fwd = 4.0 * d * P * heads
-    flop_bwd_kernel = 10.0 * d * P * heads
     useful = 14.0 * d * P * heads
     strict = 12.0 * d * P * heads
     value = useful / (ms * 1e-3) / 1e12
 
-    kernels = {k: {"launches": n, "avg_ms": t / max(n, 1)} for k, (n, t) in kt.times.items()}
-    bwd = kernels.get("bdlm_bwd")
-    fwd = kernels.get("bdlm_fwd")
+    kernels = {k: {"launches": n, "avg_ms": t / max(n, 1), "total_ms": t} for k, (n, t) in kt.times.items()}
+    # MFMA flops each kernel executes per launch (all 2*d per visible pair per
+    # product): forward S, PV; dK/dV kernel S, dP, dV, dK; dQ kernel S, dP, dQ.
+    # bdlm_bwd_pre (D = rowsum(dO * O)) is HBM-bound and small.
+    kernel_flop = {"bdlm_fwd": 4.0 * d * P * heads, "bdlm_dkdv": 8.0 * d * P * heads,
+                   "bdlm_dq": 6.0 * d * P * heads}
+    per_kernel = {}
+    for name, fl in kernel_flop.items():
+        kk = kernels.get(name)
+        if kk:
+            a = fl / (kk["avg_ms"] * 1e-3) / 1e12
+            per_kernel[name] = {"achieved": round(a, 2), "frac": round(a / PEAK_BF16_TFLOPS, 4),
+                                "avg_launch_ms": round(kk["avg_ms"], 4), "flop_per_launch": fl}
     roof = None
-    if bwd:
-        ach = flop_bwd_kernel / (bwd["avg_ms"] * 1e-3) / 1e12
-        roof = {"kernel": "bdlm_bwd", "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "flop_per_launch": flop_bwd_kernel, "avg_launch_ms": round(bwd["avg_ms"], 4)}
-    extra = {}
-    if fwd:
-        fa = flop_fwd / (fwd["avg_ms"] * 1e-3) / 1e12
-        extra["fwd_kernel"] = {"achieved": round(fa, 2), "frac": round(fa / PEAK_BF16_TFLOPS, 4),
-                               "avg_launch_ms": round(fwd["avg_ms"], 4), "flop_per_launch": flop_fwd}
+    timed = [n for n in kernel_flop if n in kernels]
+    if timed:
+        dom = max(timed, key=lambda n: kernels[n]["total_ms"])
+        pk = per_kernel[dom]
+        roof = {"kernel": dom, "bound": "mfma", "achieved": pk["achieved"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": pk["frac"], "traffic": None,
+                "flop_per_launch": pk["flop_per_launch"], "avg_launch_ms": pk["avg_launch_ms"]}
+    extra = {"kernel_roofline": per_kernel}
 
     cpu = None
     if not args.no_cpu:

@@ -81,6 +81,9 @@ Problem make_problem(const bdlm_attn_desc* d) {
   std::memset(&p, 0, sizeof(p));
   p.batch = d->batch; p.L = d->seqlen; p.B = d->block;
   p.hq = d->num_q_heads; p.hkv = d->num_kv_heads; p.group = p.hq / p.hkv; p.D = d->head_dim;
+  auto log2_exact = [](int x) { int s = 0; while ((1 << s) < x) ++s; return (1 << s) == x ? s : -1; };
+  p.bshift = log2_exact(p.B);
+  p.gshift = log2_exact(p.group);
   if (d->num_local_blocks == 0) {
     p.mode = 0;
     p.rows[0] = p.rows[1] = p.L;

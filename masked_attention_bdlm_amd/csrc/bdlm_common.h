@@ -23,6 +23,8 @@ constexpr int kWave = 64;
 // Runtime problem shape, passed by value to every kernel.
 struct Problem {
   int batch, L, B, hq, hkv, group, D;
+  int bshift;         // log2(B) when B is a power of two, else -1
+  int gshift;         // log2(group) when group is a power of two, else -1
   int mode;           // 0 = full [x0 ; xt], 1 = CSBP share (local corrupted blocks)
   int rows[2];        // query rows per stream array: full {L, L}; share {0, n*B}
   int klen[2];        // key rows per key array:      full {L, L}; share {L, n*B}
@@ -31,12 +33,20 @@ struct Problem {
   int block_ids[kMaxLocalBlocks];
 };
 
+// r / B and x / group, with shifts when the divisor is a power of two (the
+// branch is uniform across a wave).
+__host__ __device__ inline int div_b(const Problem& p, int r) { return p.bshift >= 0 ? (r >> p.bshift) : r / p.B; }
+__host__ __device__ inline int div_g(const Problem& p, int x) { return p.gshift >= 0 ? (x >> p.gshift) : x / p.group; }
+__host__ __device__ inline int mod_g(const Problem& p, int x) {
+  return p.gshift >= 0 ? (x & (p.group - 1)) : x % p.group;
+}
+
 // Visible key range [lo, hi) of query row r of stream s (0 clean, 1 corrupted /
 // local) inside key array a (0 clean, 1 corrupted / local).  lo and hi are
 // non-decreasing in r, which the schedule relies on.
 __host__ __device__ inline void row_keys(const Problem& p, int s, int r, int a, int& lo, int& hi) {
   if (p.mode == 0) {
-    const int b = r / p.B;
+    const int b = div_b(p, r);
     if (s == 0) {            // clean query: clean blocks <= b
       lo = 0;
       hi = (a == 0) ? (b + 1) * p.B : 0;
@@ -48,7 +58,7 @@ __host__ __device__ inline void row_keys(const Problem& p, int s, int r, int a, 
       hi = (b + 1) * p.B;
     }
   } else {
-    const int i = r / p.B;   // local block index
+    const int i = div_b(p, r);   // local block index
     if (a == 0) {            // clean window cut to the block's strict clean prefix
       lo = p.kv_begin;
       int e = p.block_ids[i] * p.B;
@@ -69,7 +79,7 @@ __host__ __device__ inline void row_keys(const Problem& p, int s, int r, int a, 
 // non-decreasing across blocks).
 __host__ __device__ inline void query_span(const Problem& p, int s, int a, int k0, int k1,
                                            int& r_lo, int& r_hi) {
-  const int nb = p.rows[s] / p.B;
+  const int nb = div_b(p, p.rows[s]);
   int lo, hi;
   // first block whose range ends after k0
   int x = 0, y = nb;
@@ -96,7 +106,7 @@ __host__ __device__ inline void query_span(const Problem& p, int s, int a, int k
 __host__ __device__ inline void tile_ranges(const Problem& p, int s, int a, int r0, int r1,
                                    int& klo, int& khi, int& flo, int& fhi) {
   klo = 0x7fffffff; khi = 0; flo = 0; fhi = 0x7fffffff;
-  for (int bb = r0 / p.B; bb * p.B < r1; ++bb) {
+  for (int bb = div_b(p, r0); bb * p.B < r1; ++bb) {
     int lo, hi;
     row_keys(p, s, bb * p.B, a, lo, hi);
     if (hi > lo) { klo = klo < lo ? klo : lo; khi = khi > hi ? khi : hi; }

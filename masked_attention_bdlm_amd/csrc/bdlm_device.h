@@ -91,11 +91,19 @@ template <> __device__ inline float ld_frag_crows<float>(const float* row, int c
 // tile[r0 + r/4][c0 + 4*(r%4)], lane i receives tile[r0 + j][c0 + i], j=0..3:
 // column c0 + i of rows r0..r0+3.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// The transpose-read builtin carries no alias information of its own, so the
+// compiler makes it wait for every global->LDS DMA still in flight, including
+// the one filling the other half of a double buffer.  Inlining through a
+// restrict-qualified parameter attaches alias scopes to the read, which lifts
+// that wait; the kernels order their own DMA waits and barriers explicitly.
+__device__ __forceinline__ s16x4 ds_read_tr16(const void* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(p));
+}
 __device__ inline bf16x4 ld_tr4(const bf16* tile, int stride, int r0, int c0, int i16) {
   const bf16* p = tile + (r0 + (i16 >> 2)) * stride + c0 + 4 * (i16 & 3);
-  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(p));
-  return __builtin_bit_cast(bf16x4, v);
+  return __builtin_bit_cast(bf16x4, ds_read_tr16(p));
 }
 
 __device__ inline bf16x8 cat44(bf16x4 lo, bf16x4 hi) {
@@ -155,9 +163,7 @@ template <typename T, int D> __device__ inline typename Elt<T>::Frag ld_frag_s(c
 
 template <int D> __device__ inline bf16x4 ld_tr4_s(const bf16* tile, int r0, int c0, int i16) {
   const bf16* p = tile + Swz<bf16, D>::idx(r0 + (i16 >> 2), c0 + 4 * (i16 & 3));
-  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)(p));
-  return __builtin_bit_cast(bf16x4, v);
+  return __builtin_bit_cast(bf16x4, ds_read_tr16(p));
 }
 
 // ld_frag_kcrow / ld_frag_knat on a swizzled tile.

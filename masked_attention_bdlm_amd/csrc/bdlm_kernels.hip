@@ -128,7 +128,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
   const int r0 = t * M;
   const int r1 = min(r0 + M, R);
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform per wave
   const int ln = lane & 31, hh = lane >> 5;
   const int r = r0 + 32 * w + ln;
   const bool valid = r < r1;
@@ -366,24 +367,25 @@ __device__ __forceinline__ void bwd_order(const Problem& p, int a, int ns0, int 
     int t_, hg_;                                                   \
     if (o_inter) {                                                 \
       if ((it) < o_nboth) {                                        \
-        t_ = o_thi0 - (it) / (2 * G);                              \
-        s = (((it) / G) & 1) ? o_s1 : o_s0;                        \
-        hg_ = (it) % G;                                            \
+        const int u_ = div_g(p, (it));                             \
+        t_ = o_thi0 - (u_ >> 1);                                   \
+        s = (u_ & 1) ? o_s1 : o_s0;                                \
+        hg_ = mod_g(p, (it));                                      \
       } else {                                                     \
         const int r_ = (it) - o_nboth;                             \
-        t_ = o_tb - 1 - r_ / G;                                    \
+        t_ = o_tb - 1 - div_g(p, r_);                              \
         s = o_slow;                                                \
-        hg_ = r_ % G;                                              \
+        hg_ = mod_g(p, r_);                                        \
       }                                                            \
     } else if ((it) < o_n0) {                                      \
-      t_ = o_thi0 - (it) / G;                                      \
+      t_ = o_thi0 - div_g(p, (it));                                \
       s = o_s0;                                                    \
-      hg_ = (it) % G;                                              \
+      hg_ = mod_g(p, (it));                                        \
     } else {                                                       \
       const int r_ = (it) - o_n0;                                  \
-      t_ = o_thi1 - r_ / G;                                        \
+      t_ = o_thi1 - div_g(p, r_);                                  \
       s = o_s1;                                                    \
-      hg_ = r_ % G;                                                \
+      hg_ = mod_g(p, r_);                                          \
     }                                                              \
     q0 = t_ * M;                                                   \
     h = g * G + hg_;                                               \
@@ -407,9 +409,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
   constexpr int KPL = E::KPL, KC = 2 * KPL;
   constexpr int DCH = D / KC;
   constexpr int CPS = 32 / KC;
-  __shared__ __attribute__((aligned(16))) T qd_lds[2][2][M * D];     // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float row_l[2][2][64];      // [buffer][LSE, D]
-  __shared__ int lh_l[2][2][M];                                       // [buffer][lo, hi]
+  // One LDS object (a kernel with several makes the compiler wait for every
+  // in-flight DMA into an object before any read of it, which would serialise
+  // the double buffer): [buffer][Q, dO] tiles, then [buffer][LSE, D] rows.
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * M * D * sizeof(T) + 2 * 2 * 64 * sizeof(float)];
+  T (*qd_lds)[2][M * D] = reinterpret_cast<T (*)[2][M * D]>(smem);
+  float (*row_l)[2][64] = reinterpret_cast<float (*)[2][64]>(smem + 2 * 2 * M * D * sizeof(T));
 
   const Problem& p = args.p;
   int bg, item;
@@ -420,7 +425,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
   const int k0 = args.kbase[a] + j * N;
   const int k1 = min(k0 + N, args.kend[a]);
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform per wave
   const int ln = lane & 31, hh = lane >> 5;
   const int kk = k0 + 32 * w + ln;           // this lane's key (MFMA column)
   const bool kvalid = kk < k1;
@@ -467,12 +473,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
       const float* src_ = (w == 0 ? args.lse[s_] : args.delta[s_]) + ri_;                        \
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src_,      \
                                        (__attribute__((address_space(3))) void*)(row_l[buf][w]), 4, 0, 0); \
-    }                                                                                            \
-    if (tid < M) {                                                                               \
-      int lo_ = 0, hi_ = 0;                                                                      \
-      if (q0_ + tid < q1_) row_keys(p, s_, q0_ + tid, a, lo_, hi_);                              \
-      lh_l[buf][0][tid] = lo_;                                                                   \
-      lh_l[buf][1][tid] = hi_;                                                                   \
     }                                                                                            \
   } while (0)
 
@@ -534,10 +534,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int rr0 = qs * 32 + c_row(4 * i4, hh);      // 4 consecutive rows
-        const float4 l4 = *reinterpret_cast<const float4*>(lse_r + rr0);
-        const float4 d4 = *reinterpret_cast<const float4*>(dl_r + rr0);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        // one 16-byte vector read each (a typed vector load keeps the alias
+        // information that lets the compiler skip waiting for in-flight DMA)
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_r + rr0);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(dl_r + rr0);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int i = 4 * i4 + jj;
@@ -546,11 +546,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
           de[i] = dv[jj];
         }
       }
-      if (need_mask) {
+      if (need_mask) {   // edge tiles only: visible range of each row, rows past the end masked
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int rr = qs * 32 + c_row(i, hh);
-          if (!(kk >= lh_l[cur][0][rr] && kk < lh_l[cur][1][rr])) pe[i] = 0.f;
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int row = q0 + qs * 32 + c_row(4 * i4, hh);   // 4 rows of one block
+          int lo = 0, hi = 0;
+          row_keys(p, s, min(row, R - 1), a, lo, hi);
+          const bool kin = kk >= lo && kk < hi;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (!kin || row + jj >= q1) pe[4 * i4 + jj] = 0.f;
         }
       }
       Frag pfr[CPS], sfr[CPS];
@@ -645,7 +650,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
   const int r0 = t * M;
   const int r1 = min(r0 + M, R);
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform per wave
   const int ln = lane & 31, hh = lane >> 5;
   const int r = r0 + 32 * w + ln;
   const bool valid = r < r1;
@@ -718,7 +724,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
     for (int sub = 0; sub < N / 32; ++sub) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       {
-        constexpr int BT = DCH < 4 ? DCH : 4;
+        constexpr int BT = DCH < 2 ? DCH : 2;
         Frag ka[2][BT], va[2][BT];
 #pragma unroll
         for (int c = 0; c < BT; ++c) {
