@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--workload", default="gqa_64k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -103,6 +105,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     M.load()
+    if args.copy_bytes > 0:
+        # One device-to-device copy of a known size: what the HBM byte counters
+        # read for it calibrates their reading for the attention kernels.
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes}), flush=True)
+        return
     w = WORKLOADS[args.workload]
     if w.share_blocks:
         print("share-mode workloads are measured by bench_share in the tests; use a full-mode workload",

@@ -143,17 +143,35 @@ template <> __device__ inline float ld_frag_knat<float>(const float* tile, int s
 // ---- unpadded row-major tiles with XOR-swizzled 16-byte chunks
 //
 // Row r of a D-column tile is D*sizeof(T) bytes = CH chunks of 16 bytes;
-// logical chunk c of row r is stored at chunk c ^ (r % CH).  A 16-lane read of
-// one logical chunk from 16 consecutive rows, and a transpose read of 4 rows,
-// both land on distinct LDS banks, and a row block of 1 KB is contiguous, so a
-// wave's global->LDS DMA (64 lanes x 16 bytes) fills 64/CH whole rows.
+// logical chunk c of row r is stored at chunk c ^ f(r).  A row block of 1 KB
+// stays contiguous, so a wave's global->LDS DMA (64 lanes x 16 bytes) fills
+// 64/CH whole rows whatever f is.  f is chosen for the two read patterns on
+// gfx950's 64-bank LDS (16 bank groups of 16 bytes):
+//  - a fragment read, 16 lanes reading one logical chunk of 16 consecutive
+//    rows, needs f to take 16 distinct bank groups over those rows;
+//  - a transpose read (ds_read_b64_tr_b16), half a wave reading 4 aligned
+//    chunks of 4 aligned consecutive rows, needs the 4 rows to land on 4
+//    different aligned 4-chunk groups.
+// bf16, D = 128 (CH = 16): f(r) swaps the two 2-bit halves of r mod 16.
+// bf16, D = 64 (CH = 8, two rows per 256 bytes): f(r) = g(r/2 mod 8) with g
+// moving bit 0 to bit 2.  fp32 tiles (reference precision) use f(r) = r mod CH.
 template <typename T, int D>
 struct Swz {
   static constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
   static constexpr int CH = D / EPC;                // chunks per row
   static constexpr int RPB = 64 / CH;               // rows per 1 KB DMA block
-  __device__ static inline int idx(int r, int col) {
-    return r * D + ((((col / EPC) ^ (r & (CH - 1)))) * EPC) + (col % EPC);
+  __host__ __device__ static inline int f(int r) {
+    if constexpr (sizeof(T) == 2 && CH == 16) {
+      return ((r & 3) << 2) | ((r >> 2) & 3);
+    } else if constexpr (sizeof(T) == 2 && CH == 8) {
+      const int x = (r >> 1) & 7;
+      return ((x & 1) << 2) | (x >> 1);
+    } else {
+      return r & (CH - 1);
+    }
+  }
+  __host__ __device__ static inline int idx(int r, int col) {
+    return r * D + (((col / EPC) ^ f(r)) * EPC) + (col % EPC);
   }
 };
 
@@ -196,7 +214,7 @@ __device__ inline void dma_rows(T* tile, const T* base, int64_t rs, int k0, int 
   const int lr = lane / S::CH, pc = lane % S::CH;
   for (int bb = wave; bb < NBLK; bb += nw) {
     const int r = bb * S::RPB + lr;
-    const int c = pc ^ (r & (S::CH - 1));
+    const int c = pc ^ S::f(r);
     int k = k0 + r;
     if (k >= kmax) k = kmax - 1;
     const T* src = base + (int64_t)k * rs + c * S::EPC;
