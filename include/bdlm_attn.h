@@ -119,7 +119,9 @@ int bdlm_attn_fwd(const bdlm_attn_desc* desc,
 
 /*
  * Backward with the stored-LSE recompute (P is rebuilt from Q, K and LSE):
- * D = rowsum(dO * O), then dK/dV key-major and dQ query-major (no atomics).
+ * D = rowsum(dO * O) (with LSE * log2(e), kept in the workspace: fp32
+ * [batch, Hq, rows] each, per query stream), then dK/dV key-major and dQ
+ * query-major (no atomics).
  * Full mode: inputs as the forward plus its outputs oc, ox, lse_c, lse_x and the
  *   upstream gradients doc, dox [batch, L, Hq, d].  Overwrites dqc, dqx
  *   [batch, L, Hq, d] and dkc, dvc, dkx, dvx [batch, L, Hkv, d] (all dtype).

@@ -110,7 +110,9 @@ XcdMap make_map(int nbg, int per_bg) {
 
 size_t elt_size(int dtype) { return dtype == BDLM_BF16 ? 2 : 4; }
 
-struct BwdLayout { size_t delta_off[2], total; };
+// Backward workspace: per query stream, D = rowsum(dO * O) and LSE * log2(e),
+// fp32 [batch, Hq, rows] each.
+struct BwdLayout { size_t delta_off[2], lse2_off[2], total; };
 
 BwdLayout bwd_layout(const bdlm_attn_desc* d) {
   BwdLayout l{};
@@ -118,10 +120,15 @@ BwdLayout bwd_layout(const bdlm_attn_desc* d) {
   size_t off = 0;
   if (d->num_local_blocks == 0) {
     const int64_t L = d->seqlen;
-    for (int s = 0; s < 2; ++s) { l.delta_off[s] = off; off = align256(off + sizeof(float) * B * H * L); }
+    for (int s = 0; s < 2; ++s) {
+      l.delta_off[s] = off; off = align256(off + sizeof(float) * B * H * L);
+      l.lse2_off[s] = off; off = align256(off + sizeof(float) * B * H * L);
+    }
   } else {
     const int64_t T = (int64_t)d->num_local_blocks * d->block;
     l.delta_off[0] = l.delta_off[1] = off;
+    off = align256(off + sizeof(float) * B * H * T);
+    l.lse2_off[0] = l.lse2_off[1] = off;
     off = align256(off + sizeof(float) * B * H * T);
   }
   l.total = off;
@@ -220,16 +227,18 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   const Problem p = make_problem(desc);
   char* wsb = reinterpret_cast<char*>(ws);
   float* delta[2] = {reinterpret_cast<float*>(wsb + lay.delta_off[0]), reinterpret_cast<float*>(wsb + lay.delta_off[1])};
+  float* lse2[2] = {reinterpret_cast<float*>(wsb + lay.lse2_off[0]), reinterpret_cast<float*>(wsb + lay.lse2_off[1])};
+  const float* lses[2] = {lse_c, lse_x};
   const int nbg = p.batch * p.hkv;
 
-  // 1) D = rowsum(dO * O)
+  // 1) D = rowsum(dO * O) and LSE * log2(e)
   const void* os[2] = {oc, ox};
   const void* dos[2] = {doc, dox};
   for (int s = share ? 1 : 0; s < 2; ++s) {
     BwdPreArgs pa;
     pa.batch = p.batch; pa.rows = p.rows[s]; pa.hq = p.hq; pa.D = p.D; pa.stream = s;
     pa.o = os[s]; pa.dout = dos[s]; pa.delta = delta[s];
-    pa.dq_acc = nullptr;
+    pa.lse = lses[s]; pa.lse2 = lse2[s];
     ProfScope ps("bdlm_bwd_pre", stream);
     if (launch_bwd_pre(pa, bf, stream) != hipSuccess) return BDLM_ERR_HIP;
   }
@@ -243,7 +252,7 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
     a.k[0] = kc; a.k[1] = kx;
     a.v[0] = vc; a.v[1] = vx;
     a.dout[0] = doc; a.dout[1] = dox;
-    a.lse[0] = lse_c; a.lse[1] = lse_x;
+    a.lse2[0] = lse2[0]; a.lse2[1] = lse2[1];
     a.delta[0] = delta[0]; a.delta[1] = delta[1];
     a.dk[0] = dkc; a.dk[1] = dkx;
     a.dv[0] = dvc; a.dv[1] = dvx;
@@ -280,7 +289,7 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
     a.k[0] = kc; a.k[1] = kx;
     a.v[0] = vc; a.v[1] = vx;
     a.dout[0] = doc; a.dout[1] = dox;
-    a.lse[0] = lse_c; a.lse[1] = lse_x;
+    a.lse2[0] = lse2[0]; a.lse2[1] = lse2[1];
     a.delta[0] = delta[0]; a.delta[1] = delta[1];
     a.dq[0] = dqc; a.dq[1] = dqx;
     a.scale = desc->softmax_scale;

@@ -204,15 +204,18 @@ template <> __device__ inline float ld_frag_kcrow_s<float, 64>(const float* tile
 
 // Global -> LDS DMA of rows [k0, k0+NR) of a [rows, heads, D] array (row
 // stride rs elements, pointer at the head) into a swizzled tile.  Wave `wave`
-// of `nw` issues every nw-th 1 KB block; each lane moves one 16-byte chunk.
+// of NW issues every NW-th 1 KB block; each lane moves one 16-byte chunk.
 // Rows at or past kmax re-read row kmax-1 (finite data; callers mask them).
-template <typename T, int NR, int D>
-__device__ inline void dma_rows(T* tile, const T* base, int64_t rs, int k0, int kmax, int wave, int nw, int lane) {
+template <typename T, int NR, int D, int NW = 4>
+__device__ inline void dma_rows(T* tile, const T* base, int64_t rs, int k0, int kmax, int wave, int lane) {
   using S = Swz<T, D>;
   constexpr int NBLK = NR / S::RPB;
   static_assert(NR % S::RPB == 0, "tile rows must fill whole DMA blocks");
+  static_assert(NBLK % NW == 0, "every wave issues the same number of blocks");
   const int lr = lane / S::CH, pc = lane % S::CH;
-  for (int bb = wave; bb < NBLK; bb += nw) {
+#pragma unroll
+  for (int j = 0; j < NBLK / NW; ++j) {
+    const int bb = wave + j * NW;
     const int r = bb * S::RPB + lr;
     const int c = pc ^ S::f(r);
     int k = k0 + r;
@@ -221,6 +224,15 @@ __device__ inline void dma_rows(T* tile, const T* base, int64_t rs, int k0, int 
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)(tile + bb * S::RPB * D), 16, 0, 0);
   }
+}
+
+// Return v unchanged but opaque to the compiler, held in scalar registers.
+// Kernel arguments are otherwise re-loaded from memory wherever they are used
+// (the compiler treats those loads as free to repeat), which inside a loop
+// adds a scalar-memory round trip per use.
+template <typename V> __device__ __forceinline__ V pin_sgpr(V v) {
+  asm volatile("" : "+s"(v));
+  return v;
 }
 
 // Wait until this wave's outstanding vector-memory operations (including

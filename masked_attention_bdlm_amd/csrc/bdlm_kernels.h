@@ -25,8 +25,9 @@ struct BwdPreArgs {
   int batch, rows, hq, D, stream;
   const void* o;
   const void* dout;
-  float* delta;         // [batch, hq, rows]
-  float* dq_acc;        // [batch, rows, hq, D] fp32, zeroed here (NULL = skip)
+  float* delta;         // [batch, hq, rows]: rowsum(dO * O)
+  const float* lse;     // [batch, hq, rows]: forward LSE (natural log)
+  float* lse2;          // [batch, hq, rows]: LSE * log2(e)
 };
 
 struct BwdArgs {
@@ -35,7 +36,7 @@ struct BwdArgs {
   const void* k[2];
   const void* v[2];
   const void* dout[2];
-  const float* lse[2];
+  const float* lse2[2];   // LSE * log2(e) per query stream
   const float* delta[2];
   void* dk[2];
   void* dv[2];
@@ -53,7 +54,7 @@ struct DqArgs {
   const void* k[2];
   const void* v[2];
   const void* dout[2];
-  const float* lse[2];
+  const float* lse2[2];   // LSE * log2(e) per query stream
   const float* delta[2];
   void* dq[2];          // dtype (full mode) or fp32 to add into (share mode)
   float scale, scale_log2;
@@ -79,7 +80,6 @@ hipError_t launch_fwd(const FwdArgs& a, int grid, int is_bf16, int out_f32, hipS
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t st);
 hipError_t launch_dkdv(const BwdArgs& a, int grid, int is_bf16, hipStream_t st);
 hipError_t launch_dq(const DqArgs& a, int grid, int is_bf16, int add_f32, hipStream_t st);
-hipError_t launch_convert(const float* src, void* dst, int64_t n, int is_bf16, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int out_bf16, hipStream_t st);
 
 }  // namespace bdlm

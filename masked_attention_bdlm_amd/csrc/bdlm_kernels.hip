@@ -165,8 +165,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
   }
   if (total > 0) {
     const int a0 = nt[0] > 0 ? 0 : 1;
-    dma_rows<T, N, D>(kv_lds[0][0], kb[a0], rs, klo[a0], khi[a0], w, 4, lane);
-    dma_rows<T, N, D>(kv_lds[0][1], vb[a0], rs, klo[a0], khi[a0], w, 4, lane);
+    dma_rows<T, N, D>(kv_lds[0][0], kb[a0], rs, klo[a0], khi[a0], w, lane);
+    dma_rows<T, N, D>(kv_lds[0][1], vb[a0], rs, klo[a0], khi[a0], w, lane);
   }
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -182,8 +182,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
     if (it + 1 < total) {
       const int a2 = it + 1 < nt[0] ? 0 : 1;
       const int k02 = klo[a2] + (it + 1 - (a2 ? nt[0] : 0)) * N;
-      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][0], kb[a2], rs, k02, khi[a2], w, 4, lane);
-      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, 4, lane);
+      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][0], kb[a2], rs, k02, khi[a2], w, lane);
+      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, lane);
     }
     const T* k_lds = kv_lds[it & 1][0];
     const T* v_lds = kv_lds[it & 1][1];
@@ -316,11 +316,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs args) {
     Vec16 vo = ld16(o), vd = ld16(d);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc += (float)elem_of<T>(vo, e) * (float)elem_of<T>(vd, e);
-    if (args.dq_acc) {
-      float* z = args.dq_acc + u * D + part * VEC;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) z[e] = 0.f;
-    }
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
@@ -329,7 +324,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs args) {
     const int64_t br = u / args.hq;
     const int r = (int)(br % args.rows);
     const int bb = (int)(br / args.rows);
-    args.delta[((int64_t)bb * args.hq + h) * args.rows + r] = acc;
+    const int64_t ri = ((int64_t)bb * args.hq + h) * args.rows + r;
+    args.delta[ri] = acc;
+    args.lse2[ri] = args.lse[ri] * kLog2e;
   }
   (void)s;
 }
@@ -417,6 +414,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
   float (*row_l)[2][64] = reinterpret_cast<float (*)[2][64]>(smem + 2 * 2 * M * D * sizeof(T));
 
   const Problem& p = args.p;
+  // Per-stream values read once: indexing the argument block with the
+  // iteration's stream number would re-load them from memory every iteration.
+  const int rows0 = pin_sgpr(p.rows[0]), rows1 = pin_sgpr(p.rows[1]);
+  const T* const q_0 = pin_sgpr(reinterpret_cast<const T*>(args.q[0]));
+  const T* const q_1 = pin_sgpr(reinterpret_cast<const T*>(args.q[1]));
+  const T* const do_0 = pin_sgpr(reinterpret_cast<const T*>(args.dout[0]));
+  const T* const do_1 = pin_sgpr(reinterpret_cast<const T*>(args.dout[1]));
+  const float* const l2_0 = pin_sgpr(args.lse2[0]);
+  const float* const l2_1 = pin_sgpr(args.lse2[1]);
+  const float* const dl_0 = pin_sgpr(args.delta[0]);
+  const float* const dl_1 = pin_sgpr(args.delta[1]);
   int bg, item;
   args.map.decode(blockIdx.x, bg, item);
   const int b = bg / p.hkv, g = bg % p.hkv;
@@ -461,16 +469,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
   do {                                                                                           \
     int s_, q0_, h_;                                                                             \
     BWD_DECODE(it, s_, q0_, h_);                                                                 \
-    const int R_ = p.rows[s_];                                                                   \
+    const int R_ = s_ ? rows1 : rows0;                                                                   \
     const int q1_ = min(q0_ + M, R_);                                                            \
     const int64_t hb_ = (int64_t)b * R_ * qrs + (int64_t)h_ * D;                                 \
-    dma_rows<T, M, D>(qd_lds[buf][0], reinterpret_cast<const T*>(args.q[s_]) + hb_, qrs, q0_, q1_, \
-                      w, 4, lane);                                                               \
-    dma_rows<T, M, D>(qd_lds[buf][1], reinterpret_cast<const T*>(args.dout[s_]) + hb_, qrs, q0_,   \
-                      q1_, w, 4, lane);                                                          \
+    dma_rows<T, M, D>(qd_lds[buf][0], (s_ ? q_1 : q_0) + hb_, qrs, q0_, q1_,                    \
+                      w, lane);                                                                  \
+    dma_rows<T, M, D>(qd_lds[buf][1], (s_ ? do_1 : do_0) + hb_, qrs, q0_,                        \
+                      q1_, w, lane);                                                          \
     if (w < 2) {                                                                                 \
       const int64_t ri_ = ((int64_t)b * p.hq + h_) * R_ + min(q0_ + lane, q1_ - 1);              \
-      const float* src_ = (w == 0 ? args.lse[s_] : args.delta[s_]) + ri_;                        \
+      const float* src_ = (w == 0 ? (s_ ? l2_1 : l2_0) : (s_ ? dl_1 : dl_0)) + ri_;                \
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src_,      \
                                        (__attribute__((address_space(3))) void*)(row_l[buf][w]), 4, 0, 0); \
     }                                                                                            \
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
     const int cur = it & 1;
     int s, q0, h;
     BWD_DECODE(it, s, q0, h);
-    const int R = p.rows[s];
+    const int R = s ? rows1 : rows0;
     const int q1 = min(q0 + M, R);
     int klo, khi, flo, fhi;
     tile_ranges(p, s, a, q0, q1, klo, khi, flo, fhi);
@@ -541,7 +549,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int i = 4 * i4 + jj;
-          const float e = fast_exp2(sacc[i] * sl2 - lv[jj] * kLog2e);
+          const float e = fast_exp2(sacc[i] * sl2 - lv[jj]);
           pe[i] = e;
           de[i] = dv[jj];
         }
@@ -673,7 +681,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
   float lse2 = 0.f, dd = 0.f;
   if (valid) {
     const int64_t ri = ((int64_t)b * p.hq + h) * R + r;
-    lse2 = args.lse[s][ri] * kLog2e;
+    lse2 = args.lse2[s][ri];
     dd = args.delta[s][ri];
   }
   int klo[2], khi[2], flo[2], fhi[2], nt[2], lo[2], hi[2];
@@ -694,8 +702,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
   }
   if (total > 0) {
     const int a0 = nt[0] > 0 ? 0 : 1;
-    dma_rows<T, N, D>(kv_lds[0][0], kb[a0], rs, klo[a0], khi[a0], w, 4, lane);
-    dma_rows<T, N, D>(kv_lds[0][1], vb[a0], rs, klo[a0], khi[a0], w, 4, lane);
+    dma_rows<T, N, D>(kv_lds[0][0], kb[a0], rs, klo[a0], khi[a0], w, lane);
+    dma_rows<T, N, D>(kv_lds[0][1], vb[a0], rs, klo[a0], khi[a0], w, lane);
   }
 
   f32x16 acc[D / 32];
@@ -710,8 +718,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
     if (it + 1 < total) {
       const int a2 = it + 1 < nt[0] ? 0 : 1;
       const int k02 = klo[a2] + (it + 1 - (a2 ? nt[0] : 0)) * N;
-      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][0], kb[a2], rs, k02, khi[a2], w, 4, lane);
-      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, 4, lane);
+      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][0], kb[a2], rs, k02, khi[a2], w, lane);
+      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, lane);
     }
     const T* k_lds = kv_lds[it & 1][0];
     const T* v_lds = kv_lds[it & 1][1];
@@ -804,17 +812,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
       }
     }
   }
-}
-
-// ===================================================== backward: dQ fp32 -> T
-template <typename T>
-__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ src, T* __restrict__ dst,
-                                                      int64_t n4) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const float4 v = reinterpret_cast<const float4*>(src)[i];
-  T* d = dst + i * 4;
-  d[0] = to_elt<T>(v.x); d[1] = to_elt<T>(v.y); d[2] = to_elt<T>(v.z); d[3] = to_elt<T>(v.w);
 }
 
 // ============================================================ partial merge
@@ -922,15 +919,6 @@ hipError_t launch_dq(const DqArgs& a, int grid, int is_bf16, int add_f32, hipStr
   const int D = a.p.D;
   if (is_bf16) return D == 128 ? launch_dq_t<bf16, 128>(a, grid, add_f32, st) : launch_dq_t<bf16, 64>(a, grid, add_f32, st);
   return D == 128 ? launch_dq_t<float, 128>(a, grid, add_f32, st) : launch_dq_t<float, 64>(a, grid, add_f32, st);
-}
-
-hipError_t launch_convert(const float* src, void* dst, int64_t n, int is_bf16, hipStream_t st) {
-  const int64_t n4 = n / 4;
-  const int grid = (int)((n4 + 255) / 256);
-  if (grid == 0) return hipSuccess;
-  if (is_bf16) hipLaunchKernelGGL((convert_kernel<bf16>), dim3(grid), dim3(256), 0, st, src, (bf16*)dst, n4);
-  else hipLaunchKernelGGL((convert_kernel<float>), dim3(grid), dim3(256), 0, st, src, (float*)dst, n4);
-  return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, int out_bf16, hipStream_t st) {

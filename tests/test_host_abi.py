@@ -108,11 +108,12 @@ def test_workspace_sizes():
     d = _ok_desc(batch=2, seqlen=512, hq=4, hkv=2, head_dim=128)
     assert lib.bdlm_attn_workspace_bytes(ctypes.byref(d), 0) == 0
     ws = lib.bdlm_attn_workspace_bytes(ctypes.byref(d), 1)
-    # D = rowsum(dO * O) per stream: fp32 [batch, Hq, L]; dQ needs no workspace
-    assert ws >= 2 * 4 * 2 * 4 * 512
-    assert ws < 2 * 4 * 2 * 4 * 512 + 4096
+    # D = rowsum(dO * O) and LSE * log2(e) per stream: fp32 [batch, Hq, L] each;
+    # dQ needs no workspace
+    assert ws >= 2 * 2 * 4 * 2 * 4 * 512
+    assert ws < 2 * 2 * 4 * 2 * 4 * 512 + 4096
     sd = _ok_desc(block_ids=[1, 3], kv_begin=0, kv_end=64)
-    assert lib.bdlm_attn_workspace_bytes(ctypes.byref(sd), 1) >= 4 * 4 * 32
+    assert lib.bdlm_attn_workspace_bytes(ctypes.byref(sd), 1) >= 2 * 4 * 4 * 32
     assert lib.bdlm_attn_workspace_bytes(ctypes.byref(_ok_desc(seqlen=250)), 1) == 0
 
 
