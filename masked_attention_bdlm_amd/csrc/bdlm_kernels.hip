@@ -463,12 +463,40 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
   const int G = p.group;
   const int64_t qrs = (int64_t)p.hq * D;
 
+  // Per-iteration state, decoded 64 iterations at a time (one per lane, as
+  // vector code) and packed: query tile | stream << 19 | mask << 20 |
+  // head-in-group << 21.  An iteration then costs two lane reads instead of
+  // the branchy scalar decode, which all waves of the CU would otherwise run
+  // on the shared scalar unit.
+#define DKDV_ENTRY(idx, out)                                                                     \
+  do {                                                                                           \
+    int s_e, q0_e, h_e;                                                                          \
+    BWD_DECODE(idx, s_e, q0_e, h_e);                                                             \
+    const int R_e = s_e ? rows1 : rows0;                                                         \
+    const int q1_e = min(q0_e + M, R_e);                                                         \
+    int klo_e, khi_e, flo_e, fhi_e;                                                              \
+    tile_ranges(p, s_e, a, q0_e, q1_e, klo_e, khi_e, flo_e, fhi_e);                              \
+    const unsigned m_e = (!(k0 >= flo_e && k0 + N <= fhi_e) || (q1_e - q0_e < M)) ? 1u : 0u;    \
+    out = (unsigned)(q0_e / M) | ((unsigned)s_e << 19) | (m_e << 20) | ((unsigned)(h_e - g * G) << 21); \
+  } while (0)
+  unsigned ent0 = 0, ent1 = 0;
+  int ent_base = 0;
+  if (total > 0) {
+    DKDV_ENTRY(min(lane, total - 1), ent0);
+    DKDV_ENTRY(min(64 + lane, total - 1), ent1);
+  }
+#define DKDV_GET(x)                                                                \
+  ((x) - ent_base < 64 ? (unsigned)__builtin_amdgcn_readlane((int)ent0, (x) - ent_base) \
+                       : (unsigned)__builtin_amdgcn_readlane((int)ent1, (x) - ent_base - 64))
+
   // DMA of iteration `it`'s Q/dO tiles and row data into buffer `buf`; rows past
   // the stream end re-read its last row and are masked in the main block.
 #define DKDV_ISSUE(it, buf)                                                                      \
   do {                                                                                           \
-    int s_, q0_, h_;                                                                             \
-    BWD_DECODE(it, s_, q0_, h_);                                                                 \
+    const unsigned e_ = DKDV_GET(it);                                                            \
+    const int s_ = (int)((e_ >> 19) & 1u);                                                       \
+    const int q0_ = (int)(e_ & 0x7FFFFu) * M;                                                    \
+    const int h_ = g * G + (int)(e_ >> 21);                                                      \
     const int R_ = s_ ? rows1 : rows0;                                                                   \
     const int q1_ = min(q0_ + M, R_);                                                            \
     const int64_t hb_ = (int64_t)b * R_ * qrs + (int64_t)h_ * D;                                 \
@@ -488,13 +516,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
   const float sl2 = args.scale_log2;
   for (int it = 0; it < total; ++it) {
     const int cur = it & 1;
-    int s, q0, h;
-    BWD_DECODE(it, s, q0, h);
+    if (it - ent_base == 64) {   // next 64 decoded iterations
+      ent0 = ent1;
+      ent_base += 64;
+      DKDV_ENTRY(min(ent_base + 64 + lane, total - 1), ent1);
+    }
+    const unsigned e = DKDV_GET(it);
+    const int s = (int)((e >> 19) & 1u);
+    const int q0 = (int)(e & 0x7FFFFu) * M;
     const int R = s ? rows1 : rows0;
     const int q1 = min(q0 + M, R);
-    int klo, khi, flo, fhi;
-    tile_ranges(p, s, a, q0, q1, klo, khi, flo, fhi);
-    const bool need_mask = !(k0 >= flo && k0 + N <= fhi) || (q1 - q0 < M);
+    const bool need_mask = (e >> 20) & 1u;
     wait_vmem();
     __syncthreads();   // buffer `cur` holds iteration it; buffer cur^1 is free
     if (it + 1 < total) DKDV_ISSUE(it + 1, cur ^ 1);
@@ -608,6 +640,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
     }
   }
 #undef DKDV_ISSUE
+#undef DKDV_GET
+#undef DKDV_ENTRY
 
   // dK = scale * sum dS^T Q, dV = sum P^T dO for the wave's 32 keys.
   T* dkb = reinterpret_cast<T*>(args.dk[a]) + (int64_t)b * p.klen[a] * krs + (int64_t)g * D;
