@@ -235,6 +235,20 @@ template <typename V> __device__ __forceinline__ V pin_sgpr(V v) {
   return v;
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's own LDS
+// reads and writes (lgkmcnt(0)), not for its outstanding global->LDS DMA, so
+// prefetches stay in flight across it.  __syncthreads() would also wait for
+// the DMA (its release fence must cover every LDS write, DMA included).  A
+// tile written by DMA is published by its issuing wave waiting for it
+// (s_waitcnt vmcnt) before the barrier.  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wait until this wave's outstanding vector-memory operations (including
 // global->LDS DMA) have completed: s_waitcnt vmcnt(0).
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -660,6 +660,284 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
   }
 }
 
+// ================================= backward: dK/dV kernel, bf16, two roles
+// Eight waves, two per SIMD, in four pairs; pair w owns keys k0 + 32w .. +31
+// of the workgroup's 128-key tile.  The producer wave (w) keeps K_w, V_w in
+// registers and, per 32-row query sub-tile, computes S = Q K_w^T and
+// dP = dO V_w^T (MFMA), then P = exp2(S * scale * log2e - LSE * log2e) and
+// dS = P (dP - D) (VALU), and hands P and dS, already packed as bf16 MFMA
+// operands, to its consumer wave (w + 4) through LDS.  The consumer keeps dK_w
+// and dV_w in registers and accumulates dV += P^T dO and dK += dS^T Q with dO
+// and Q read transposed out of the tiles.  Step j runs the producers on
+// sub-tile j and the consumers on sub-tile j - 1, so on each SIMD one wave's
+// exponentials overlap the other's MFMAs; a workgroup barrier ends each step.
+// Q/dO tiles with their LSE and D rows are triple-buffered; the consumers'
+// global->LDS DMA fills tile i during steps 2i-3 .. 2i-1.
+template <int D>
+struct DkdvWs {
+  static constexpr int M = 64;                         // query rows per tile
+  static constexpr int DCH = D / 16;                   // 16-wide k chunks
+  static constexpr int DT = D / 32;                    // 32-column blocks
+  static constexpr int TILE = M * D * 2;               // one Q or dO tile (bytes)
+  static constexpr int BUFB = 2 * TILE + 512;          // Q, dO, LSE*log2e[64], D[64]
+  static constexpr int NBUF = 3;
+  static constexpr int PDS = NBUF * BUFB;              // P/dS exchange area
+  static constexpr int SLOT = 4 * 4 * 1024;            // 4 pairs x {P0, P1, dS0, dS1} x 64 lanes x 16 B
+  static constexpr int BYTES = PDS + 2 * SLOT;
+};
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
+  using L = DkdvWs<D>;
+  constexpr int N = 128, M = L::M;
+  static_assert(L::BYTES <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+
+  const Problem& p = args.p;
+  const int rows0 = pin_sgpr(p.rows[0]), rows1 = pin_sgpr(p.rows[1]);
+  const bf16* const q_0 = pin_sgpr(reinterpret_cast<const bf16*>(args.q[0]));
+  const bf16* const q_1 = pin_sgpr(reinterpret_cast<const bf16*>(args.q[1]));
+  const bf16* const do_0 = pin_sgpr(reinterpret_cast<const bf16*>(args.dout[0]));
+  const bf16* const do_1 = pin_sgpr(reinterpret_cast<const bf16*>(args.dout[1]));
+  const float* const l2_0 = pin_sgpr(args.lse2[0]);
+  const float* const l2_1 = pin_sgpr(args.lse2[1]);
+  const float* const dl_0 = pin_sgpr(args.delta[0]);
+  const float* const dl_1 = pin_sgpr(args.delta[1]);
+  int bg, item;
+  args.map.decode(blockIdx.x, bg, item);
+  const int b = bg / p.hkv, g = bg % p.hkv;
+  const int a = item < args.nkt[0] ? 0 : 1;
+  const int jt = a == 0 ? item : item - args.nkt[0];
+  const int k0 = args.kbase[a] + jt * N;
+  const int k1 = min(k0 + N, args.kend[a]);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = w & 3;
+  const bool producer = w < 4;
+  const int ln = lane & 31, hh = lane >> 5;
+  const int kk = k0 + 32 * pair + ln;        // this lane's key (MFMA column)
+  const bool kvalid = kk < k1;
+  const int64_t krs = (int64_t)p.hkv * D;
+  const int64_t qrs = (int64_t)p.hq * D;
+
+  int o[12];
+  bwd_order(p, a, args.ns0, k0, k1, M, o);
+  const int o_s0 = o[0], o_s1 = o[1], o_thi0 = o[3], o_thi1 = o[5], o_inter = o[6], o_tb = o[7];
+  const int o_slow = o[8], o_nboth = o[9], o_n0 = o[10], total = o[11];
+  const int G = p.group;
+
+  // Iteration (tile) i's state, decoded 64 at a time, one per lane:
+  // query tile | stream << 19 | mask << 20 | head-in-group << 21.
+  unsigned ent = 0;
+  int ent_base = 0;
+#define WS_ENTRY(idx, out)                                                                       \
+  do {                                                                                           \
+    int s_e, q0_e, h_e;                                                                          \
+    BWD_DECODE(idx, s_e, q0_e, h_e);                                                             \
+    const int R_e = s_e ? rows1 : rows0;                                                         \
+    const int q1_e = min(q0_e + M, R_e);                                                         \
+    int klo_e, khi_e, flo_e, fhi_e;                                                              \
+    tile_ranges(p, s_e, a, q0_e, q1_e, klo_e, khi_e, flo_e, fhi_e);                              \
+    const unsigned m_e = (!(k0 >= flo_e && k0 + N <= fhi_e) || (q1_e - q0_e < M)) ? 1u : 0u;    \
+    out = (unsigned)(q0_e / M) | ((unsigned)s_e << 19) | (m_e << 20) | ((unsigned)(h_e - g * G) << 21); \
+  } while (0)
+  // entry of tile x; x never decreases between calls of one wave
+#define WS_GET(x, out)                                                                           \
+  do {                                                                                           \
+    if ((x) - ent_base >= 64) {                                                                  \
+      ent_base = (x);                                                                            \
+      WS_ENTRY(min(ent_base + lane, total - 1), ent);                                            \
+    }                                                                                            \
+    out = (unsigned)__builtin_amdgcn_readlane((int)ent, (x) - ent_base);                         \
+  } while (0)
+  if (total > 0) WS_ENTRY(min(lane, total - 1), ent);
+
+  if (producer) {
+    // ------------------------------------------------------------ producer
+    const bf16* kbase = reinterpret_cast<const bf16*>(args.k[a]) + (int64_t)b * p.klen[a] * krs + (int64_t)g * D;
+    const bf16* vbase = reinterpret_cast<const bf16*>(args.v[a]) + (int64_t)b * p.klen[a] * krs + (int64_t)g * D;
+    bf16x8 kf[L::DCH], vf[L::DCH];
+#pragma unroll
+    for (int c = 0; c < L::DCH; ++c) {
+      const int64_t off = (int64_t)(kvalid ? kk : k0) * krs + c * 16 + hh * 8;
+      kf[c] = ld_frag<bf16>(kbase + off);
+      vf[c] = ld_frag<bf16>(vbase + off);
+      if (!kvalid) { kf[c] = bf16x8{}; vf[c] = bf16x8{}; }
+    }
+    uint32_t offA[L::DCH];
+#pragma unroll
+    for (int c = 0; c < L::DCH; ++c) offA[c] = 2u * (uint32_t)Swz<bf16, D>::idx(ln, (2 * c + hh) * 8);
+    const float sl2 = args.scale_log2;
+    barrier_lds();                                  // tile 0 has landed
+    for (int j = 0; j <= 2 * total; ++j) {
+      if (j < 2 * total) {
+        const int it = j >> 1, qs = j & 1;
+        const char* tb = smem + (it % L::NBUF) * L::BUFB;
+        unsigned e;
+        WS_GET(it, e);
+        // S and dP for rows qs*32 .. +31 (rows = queries, column = this lane's key)
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+        for (int c = 0; c < L::DCH; ++c) {
+          const char* ap = tb + offA[c] + qs * 32 * D * 2;
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(ap);
+          const bf16x8 da = *reinterpret_cast<const bf16x8*>(ap + L::TILE);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[c], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[c], pacc, 0, 0, 0);
+        }
+        // P and dS in the C layout (k of the consumer's MFMAs = queries)
+        const char* rb = tb + 2 * L::TILE;
+        float pe[16], de[16];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int rr = qs * 32 + 8 * i4 + 4 * hh;
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(rb + rr * 4);
+          const f32x4 dv = *reinterpret_cast<const f32x4*>(rb + 256 + rr * 4);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int i = 4 * i4 + jj;
+            const float ex = fast_exp2(__builtin_fmaf(sacc[i], sl2, -lv[jj]));
+            pe[i] = ex;
+            de[i] = ex * (pacc[i] - dv[jj]);
+          }
+        }
+        if ((e >> 20) & 1u) {   // edge tile: each row's visible keys; rows past the stream end
+          const int s = (int)((e >> 19) & 1u);
+          const int q0 = (int)(e & 0x7FFFFu) * M;
+          const int R = s ? rows1 : rows0;
+          const int q1 = min(q0 + M, R);
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int row = q0 + qs * 32 + 8 * i4 + 4 * hh;
+            int lo = 0, hi = 0;
+            row_keys(p, s, min(row, R - 1), a, lo, hi);
+            const bool kin = kk >= lo && kk < hi;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              if (!kin || row + jj >= q1) { pe[4 * i4 + jj] = 0.f; de[4 * i4 + jj] = 0.f; }
+          }
+        }
+        char* pd = smem + L::PDS + (j & 1) * L::SLOT + pair * 4096 + lane * 16;
+#pragma unroll
+        for (int ci = 0; ci < 2; ++ci) {
+          *reinterpret_cast<bf16x8*>(pd + ci * 1024) = pack_frag<bf16>(&pe[8 * ci]);
+          *reinterpret_cast<bf16x8*>(pd + 2048 + ci * 1024) = pack_frag<bf16>(&de[8 * ci]);
+        }
+      }
+      barrier_lds();
+    }
+  } else {
+    // ------------------------------------------------------------ consumer
+    const int wy = w - 4;
+    uint32_t offT[2 * L::DT];
+    {
+      const int i16 = lane & 15;
+#pragma unroll
+      for (int dt = 0; dt < L::DT; ++dt) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int r = 4 * hh + 8 * h2 + (i16 >> 2);
+          const int col = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+          offT[2 * dt + h2] = 2u * (uint32_t)Swz<bf16, D>::idx(r, col);
+        }
+      }
+    }
+    f32x16 dkacc[L::DT], dvacc[L::DT];
+#pragma unroll
+    for (int dt = 0; dt < L::DT; ++dt) { dkacc[dt] = f32x16{}; dvacc[dt] = f32x16{}; }
+    // DMA of tile i: 4 Q blocks, 4 dO blocks per wave (+ the LSE / D row for
+    // consumers 0 and 1); rows past the stream end re-read its last row.
+#define WS_ISSUE(i)                                                                              \
+  do {                                                                                           \
+    unsigned e_;                                                                                 \
+    WS_GET(i, e_);                                                                               \
+    const int s_ = (int)((e_ >> 19) & 1u);                                                       \
+    const int q0_ = (int)(e_ & 0x7FFFFu) * M;                                                    \
+    const int h_ = g * G + (int)(e_ >> 21);                                                      \
+    const int R_ = s_ ? rows1 : rows0;                                                           \
+    const int q1_ = min(q0_ + M, R_);                                                            \
+    const int64_t hb_ = (int64_t)b * R_ * qrs + (int64_t)h_ * D;                                 \
+    bf16* tq_ = reinterpret_cast<bf16*>(smem + ((i) % L::NBUF) * L::BUFB);                       \
+    dma_rows<bf16, M, D>(tq_, (s_ ? q_1 : q_0) + hb_, qrs, q0_, q1_, wy, lane);                  \
+    dma_rows<bf16, M, D>(tq_ + M * D, (s_ ? do_1 : do_0) + hb_, qrs, q0_, q1_, wy, lane);        \
+    if (wy < 2) {                                                                                \
+      const int64_t ri_ = ((int64_t)b * p.hq + h_) * R_ + min(q0_ + lane, q1_ - 1);              \
+      const float* src_ = (wy == 0 ? (s_ ? l2_1 : l2_0) : (s_ ? dl_1 : dl_0)) + ri_;             \
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src_,      \
+                                       (__attribute__((address_space(3))) void*)(smem +          \
+                                           ((i) % L::NBUF) * L::BUFB + 2 * L::TILE + wy * 256), 4, 0, 0); \
+    }                                                                                            \
+  } while (0)
+    // vector-memory operations one tile's DMA leaves outstanding in this wave
+#define WS_WAIT_BUT_ONE_TILE()                                                                   \
+  do {                                                                                           \
+    if (wy < 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (M / Swz<bf16, D>::RPB) / 4 + 1));      \
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (M / Swz<bf16, D>::RPB) / 4));                 \
+  } while (0)
+    if (total > 0) WS_ISSUE(0);
+    if (total > 1) { WS_ISSUE(1); WS_WAIT_BUT_ONE_TILE(); } else wait_vmem();
+    barrier_lds();                                  // tile 0 has landed
+    for (int j = 0; j <= 2 * total; ++j) {
+      if ((j & 1) && (j + 3) / 2 < total) WS_ISSUE((j + 3) / 2);
+      if (j >= 1) {
+        const int jj = j - 1;
+        const int qs = jj & 1;
+        const char* tb = smem + ((jj >> 1) % L::NBUF) * L::BUFB;
+        const char* pd = smem + L::PDS + (jj & 1) * L::SLOT + pair * 4096 + lane * 16;
+        bf16x8 pfr[2], sfr[2];
+#pragma unroll
+        for (int ci = 0; ci < 2; ++ci) {
+          pfr[ci] = *reinterpret_cast<const bf16x8*>(pd + ci * 1024);
+          sfr[ci] = *reinterpret_cast<const bf16x8*>(pd + 2048 + ci * 1024);
+        }
+        // dV_w += P^T dO ; dK_w += dS^T Q
+#pragma unroll
+        for (int dt = 0; dt < L::DT; ++dt) {
+#pragma unroll
+          for (int ci = 0; ci < 2; ++ci) {
+            const int imm = (qs * 32 + 16 * ci) * D * 2;
+            const char* b0 = tb + offT[2 * dt] + imm;
+            const char* b1 = tb + offT[2 * dt + 1] + imm;
+            const bf16x8 ob = cat44(__builtin_bit_cast(bf16x4, ds_read_tr16(b0 + L::TILE)),
+                                    __builtin_bit_cast(bf16x4, ds_read_tr16(b1 + L::TILE)));
+            const bf16x8 qb = cat44(__builtin_bit_cast(bf16x4, ds_read_tr16(b0)),
+                                    __builtin_bit_cast(bf16x4, ds_read_tr16(b1)));
+            dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfr[ci], ob, dvacc[dt], 0, 0, 0);
+            dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sfr[ci], qb, dkacc[dt], 0, 0, 0);
+          }
+        }
+      }
+      if (j & 1) {                                    // tile (j+1)/2 is read from step j+1 on
+        const int i = (j + 1) / 2;
+        if (i < total) {
+          if (i + 1 < total) WS_WAIT_BUT_ONE_TILE(); else wait_vmem();
+        }
+      }
+      barrier_lds();
+    }
+#undef WS_ISSUE
+#undef WS_WAIT_BUT_ONE_TILE
+    // dK = scale * sum dS^T Q, dV = sum P^T dO for the pair's 32 keys
+    bf16* dkb = reinterpret_cast<bf16*>(args.dk[a]) + (int64_t)b * p.klen[a] * krs + (int64_t)g * D;
+    bf16* dvb = reinterpret_cast<bf16*>(args.dv[a]) + (int64_t)b * p.klen[a] * krs + (int64_t)g * D;
+#pragma unroll
+    for (int dt = 0; dt < L::DT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 32 * pair + c_row(i, hh);
+        if (key < k1) {
+          const int64_t off = (int64_t)key * krs + dt * 32 + ln;
+          dkb[off] = to_elt<bf16>(dkacc[dt][i] * args.scale);
+          dvb[off] = to_elt<bf16>(dvacc[dt][i]);
+        }
+      }
+    }
+  }
+#undef WS_GET
+#undef WS_ENTRY
+}
+
 // ======================================================== backward: dQ kernel
 // Query-major: one workgroup per (batch, q-head, stream, 128-row query tile),
 // the forward's decomposition.  Per key tile it recomputes S^T = K Q^T and
@@ -933,8 +1211,8 @@ hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t st) {
 hipError_t launch_dkdv(const BwdArgs& a, int grid, int is_bf16, hipStream_t st) {
   const int D = a.p.D;
   if (is_bf16) {
-    if (D == 128) hipLaunchKernelGGL((dkdv_kernel<bf16, 128>), dim3(grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dkdv_kernel<bf16, 64>), dim3(grid), dim3(256), 0, st, a);
+    if (D == 128) hipLaunchKernelGGL((dkdv_ws_kernel<128>), dim3(grid), dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((dkdv_ws_kernel<64>), dim3(grid), dim3(512), 0, st, a);
   } else {
     if (D == 128) hipLaunchKernelGGL((dkdv_kernel<float, 128>), dim3(grid), dim3(256), 0, st, a);
     else hipLaunchKernelGGL((dkdv_kernel<float, 64>), dim3(grid), dim3(256), 0, st, a);
