@@ -27,6 +27,37 @@ PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+# HBM bytes per launch of the dominant kernel, from rocprofv3 --pmc FETCH_SIZE
+# and WRITE_SIZE (KiB per dispatch) on one step of the default workload, each
+# scaled by what the same counter reads for a 1 GiB device copy (FETCH_SIZE
+# reads 0.5 GiB there: x2.0; WRITE_SIZE 1 GiB: x1.0).  Valid only for the
+# kernel sources with this SHA-256; after any change the field is null until
+# the counters are taken again.
+MEASURED_TRAFFIC = {
+    "kernel": "bdlm_dkdv",
+    "sources_sha256": "ea79f824dd86b8d9fe827c90191824bc96a04d7153110bfa557ea13f16eea090",
+    "fetch_kib": 1.46e7, "fetch_scale": 2.0,
+    "write_kib": 2.622e5, "write_scale": 1.0,
+}
+KERNEL_SOURCES = ["bdlm_kernels.hip", "bdlm_kernels.h", "bdlm_device.h", "bdlm_common.h"]
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "masked_attention_bdlm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    m = MEASURED_TRAFFIC
+    if kernel != m["kernel"] or kernel_sources_sha256() != m["sources_sha256"]:
+        return None
+    return 1024.0 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"])
+
+
 def visible_pairs(L, B):
     n = L // B
     return B * B * n * (n + 1)
@@ -36,7 +67,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, x, seconds_budget=20.0, max_units=64):
+def cpu_baseline(w, x, seconds_budget=15.0, max_units=1024):
     """Time the fp64 oracle on sampled units of the same workload (bounded)."""
     import torch
     from threadpoolctl import threadpool_info
@@ -86,7 +117,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa_64k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter calibration)")
     args = ap.parse_args()
@@ -179,8 +210,11 @@ def main():
     if timed:
         dom = max(timed, key=lambda n: kernels[n]["total_ms"])
         pk = per_kernel[dom]
+        traffic = measured_traffic(dom)
         roof = {"kernel": dom, "bound": "mfma", "achieved": pk["achieved"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": pk["frac"], "traffic": None,
+                "unit": "TFLOP/s", "frac": pk["frac"],
+                "traffic": None if traffic is None else round(traffic),
+                "traffic_unit": "bytes per launch (HBM, counter-calibrated)",
                 "flop_per_launch": pk["flop_per_launch"], "avg_launch_ms": pk["avg_launch_ms"]}
     extra = {"kernel_roofline": per_kernel}
 
