@@ -179,12 +179,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
     const int k0 = klo[a] + (it - (a ? nt[0] : 0)) * N;
     wait_vmem();
     __syncthreads();   // tile `it` is in buffer it&1; buffer (it+1)&1 is free
-    if (it + 1 < total) {
-      const int a2 = it + 1 < nt[0] ? 0 : 1;
-      const int k02 = klo[a2] + (it + 1 - (a2 ? nt[0] : 0)) * N;
-      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][0], kb[a2], rs, k02, khi[a2], w, lane);
-      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, lane);
-    }
     const T* k_lds = kv_lds[it & 1][0];
     const T* v_lds = kv_lds[it & 1][1];
     const bool need_mask = !(k0 >= flo[a] && k0 + N <= fhi[a]);
@@ -216,6 +210,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // Next tile's DMA, issued behind the S^T MFMAs: a wave stalls while the
+    // memory pipeline accepts its DMA instructions, which then overlaps the
+    // matrix core working through those MFMAs.
+    if (it + 1 < total) {
+      const int a2 = it + 1 < nt[0] ? 0 : 1;
+      const int k02 = klo[a2] + (it + 1 - (a2 ? nt[0] : 0)) * N;
+      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][0], kb[a2], rs, k02, khi[a2], w, lane);
+      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     float mx = -INFINITY;
 #pragma unroll
@@ -1027,12 +1031,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
     const int k0 = klo[a] + (it - (a ? nt[0] : 0)) * N;
     wait_vmem();
     __syncthreads();   // tile `it` is in buffer it&1; buffer (it+1)&1 is free
-    if (it + 1 < total) {
-      const int a2 = it + 1 < nt[0] ? 0 : 1;
-      const int k02 = klo[a2] + (it + 1 - (a2 ? nt[0] : 0)) * N;
-      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][0], kb[a2], rs, k02, khi[a2], w, lane);
-      dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, lane);
-    }
     const T* k_lds = kv_lds[it & 1][0];
     const T* v_lds = kv_lds[it & 1][1];
     const bool need_mask = !(k0 >= flo[a] && k0 + N <= fhi[a]) || (r1 - r0 < M);
@@ -1070,6 +1068,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // Next tile's DMA, issued behind the first sub-tile's S^T / dP^T MFMAs
+      // (a wave stalls while the memory pipeline accepts DMA instructions).
+      if (sub == 0 && it + 1 < total) {
+        const int a2 = it + 1 < nt[0] ? 0 : 1;
+        const int k02 = klo[a2] + (it + 1 - (a2 ? nt[0] : 0)) * N;
+        dma_rows<T, N, D>(kv_lds[(it + 1) & 1][0], kb[a2], rs, k02, khi[a2], w, lane);
+        dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       Frag dsf[CPS];
 #pragma unroll
       for (int ci = 0; ci < CPS; ++ci) {
