@@ -9,6 +9,11 @@ value = useful TFLOP/s = 14 * d * P * batch * Hq / time, P = L(L+B) visible
 (query, key) pairs per (batch, q-head) (masked pairs excluded; the backward
 counts 2.5x the forward, i.e. its S recompute).  One JSON line is printed.
 
+--workload csbp_share_256k times one rank's CSBP share instead: 16 corrupted
+blocks of 1024 against a 262144-token clean sequence streamed in 8192-token
+chunks with the running merge, forward and backward (P = sum of B^2 (b_i + 1)
+over the local blocks), plus the merge kernel alone on every partial of a step.
+
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 """
 import argparse
@@ -110,6 +115,110 @@ def cpu_baseline(w, x, seconds_budget=15.0, max_units=1024):
     }
 
 
+def time_steps(step, steps, warmup, launches_per_step):
+    """Warm up, then time `steps` steps: wall clock bracketed by device
+    synchronisation (the reported rate), per-step HIP events on the stream
+    (median / min), and per-kernel launch times recorded by the library."""
+    import torch
+    import masked_attention_bdlm_amd as M
+    for i in range(warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{warmup} done")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    with M.KernelTimer(max_launches=launches_per_step * steps + 16) as kt:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record()
+            step()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    per_step = sorted(a.elapsed_time(b_) for a, b_ in ev)
+    log(f"timed {steps} steps: {ms:.3f} ms/step (median {per_step[len(per_step) // 2]:.3f}, min {per_step[0]:.3f})")
+    return ms, per_step, kt
+
+
+def step_stats(per_step):
+    return {"median_ms": round(per_step[len(per_step) // 2], 4), "min_ms": round(per_step[0], 4)}
+
+
+def bench_share(args, w, dev, stream):
+    """One rank's CSBP share at its real shape: own-block partial, clean chunks
+    streamed with an in-place running merge, then the chunked backward.  Also
+    times one all-at-once merge of every partial a step produces (the merge
+    kernel alone, HBM-bound)."""
+    import torch
+    from masked_attention_bdlm_amd.api import bdlm_attn_merge_partials
+    from masked_attention_bdlm_amd.csbp import ShareBuffers, _chunks, share_backward, share_forward
+    from synth import make_share_inputs
+
+    x = make_share_inputs(w, device=dev)
+    ids = [int(i) for i in x["block_ids"]]
+    B, L, d, hq = w.block, w.seqlen, w.head_dim, w.hq
+    T = len(ids) * B
+    log(f"workload {w.name}: {len(ids)} local blocks of {B} at ids {ids}, clean L {L}, chunk {w.share_chunk}")
+    bufs = ShareBuffers(x["qx"], x["kc"], x["kx"])
+    torch.cuda.synchronize()
+
+    def step():
+        o, lse = share_forward(x["qx"], x["kx"], x["vx"], x["kc"], x["vc"], ids, B, w.share_chunk,
+                               w.scale, bufs, stream)
+        share_backward(x["qx"], x["kx"], x["vx"], x["kc"], x["vc"], ids, B, w.share_chunk, o, lse,
+                       x["dox"], w.scale, bufs, stream)
+
+    nchunks = len(_chunks(L, w.share_chunk, ids, B))
+    ms, per_step, kt = time_steps(step, args.steps, args.warmup, launches_per_step=8 * nchunks + 16)
+    pairs = sum(B * B * (bid + 1) for bid in ids)        # clean prefix b_i*B plus the own block
+    useful = 14.0 * d * pairs * hq
+    kernels = {k: {"launches": n, "avg_ms": tt / max(n, 1), "total_ms": tt} for k, (n, tt) in kt.times.items()}
+
+    # merge kernel alone: all nchunks + 1 partials of a step merged at once into bf16
+    nparts = nchunks + 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    po = [torch.randn((1, T, hq, d), device=dev, generator=g) for _ in range(nparts)]
+    pl = [torch.randn((1, hq, T), device=dev, generator=g) for _ in range(nparts)]
+    mo = torch.empty((1, T, hq, d), dtype=x["qx"].dtype, device=dev)
+    ml = torch.empty((1, hq, T), dtype=torch.float32, device=dev)
+    bdlm_attn_merge_partials(po, pl, mo, ml, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        bdlm_attn_merge_partials(po, pl, mo, ml, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    mms = e0.elapsed_time(e1) / reps
+    mbytes = T * hq * (nparts * (4 * d + 4) + (mo.element_size() * d + 4))
+    out = {
+        "metric": "BDLM attn CSBP share (one rank's corrupted blocks vs the streamed clean prefix) "
+                  "fwd+bwd useful TFLOP/s, 1 GPU",
+        "value": round(useful / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), **step_stats(per_step),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "clean_len": L, "block": B, "local_blocks": len(ids),
+                   "block_ids": ids, "chunk": w.share_chunk, "chunks": nchunks, "q_heads": hq,
+                   "kv_heads": w.hkv, "head_dim": d, "parallelism": "single GPU (one rank's share)"},
+        "pct_of_peak": round(100.0 * useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "useful_flop_per_step": useful,
+        "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in kernels.items()},
+        "kernel_launches_per_step": {k: v["launches"] // args.steps for k, v in kernels.items()},
+        "merge_alone": {"parts": nparts, "rows": T, "heads": hq, "bytes": mbytes, "ms": round(mms, 4),
+                        "achieved_GBps": round(mbytes / (mms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(mbytes / (mms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,11 +256,11 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes}), flush=True)
         return
     w = WORKLOADS[args.workload]
-    if w.share_blocks:
-        print("share-mode workloads are measured by bench_share in the tests; use a full-mode workload",
-              file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    if w.share_blocks:
+        bench_share(args, w, dev, stream)
+        return
     log(f"workload {w.name}: batch {w.batch} L {w.seqlen} B {w.block} hq {w.hq} hkv {w.hkv} d {w.head_dim}")
     x = make_full_inputs(w, device=dev)
     torch.cuda.synchronize()
@@ -163,7 +272,6 @@ def main():
     dqc, dqx = torch.empty_like(x["qc"]), torch.empty_like(x["qx"])
     dkc, dvc, dkx, dvx = (torch.empty_like(x["kc"]) for _ in range(4))
     ws = workspace(desc, True, dev)
-    stream = torch.cuda.current_stream(dev)
 
     def step():
         bdlm_attn_fwd(desc, x["qc"], x["kc"], x["vc"], x["qx"], x["kx"], x["vx"], oc, ox, lse_c, lse_x,
@@ -171,20 +279,7 @@ def main():
         bdlm_attn_bwd(desc, x["qc"], x["kc"], x["vc"], x["qx"], x["kx"], x["vx"], oc, ox, lse_c, lse_x,
                       x["doc"], x["dox"], dqc, dkc, dvc, dqx, dkx, dvx, ws, stream)
 
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        log(f"warmup step {i + 1}/{args.warmup} done")
-
-    torch.cuda.synchronize()
-    with M.KernelTimer(max_launches=16 * args.steps + 16) as kt:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+    ms, per_step, kt = time_steps(step, args.steps, args.warmup, launches_per_step=16)
 
     P = visible_pairs(w.seqlen, w.block)
     heads = w.batch * w.hq
@@ -231,6 +326,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        **step_stats(per_step),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
