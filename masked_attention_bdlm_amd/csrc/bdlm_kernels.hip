@@ -1150,34 +1150,68 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs args) {
   const int64_t li = (bb * args.heads + h) * args.tokens + t;
   const int64_t oi = row * D + part * 4;
 
+  // Pass 1: the row's LPR lanes read the parts' LSEs in parallel (lane `part`
+  // reads parts part, part + LPR, ...), then a shuffle reduction gives the max
+  // and a ballot the set of live parts (LSE > -inf).  The LSE values stay
+  // cached for pass 2.
+  const int lane = threadIdx.x & 63;
+  const int gbase = lane & ~(LPR - 1);          // first lane of this row's group
   float m = -INFINITY;
-  int live = 0;
-  for (int j = 0; j < args.nparts; ++j) {
-    const float l = args.lse[j][li];
+  uint64_t live = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxMergeParts / LPR; ++k) {
+    const int jj = part + k * LPR;
+    const float l = jj < args.nparts ? args.lse[jj][li] : -INFINITY;
     m = fmaxf(m, l);
-    live += (j > 0 && l != -INFINITY);
+    const uint64_t bal = __ballot(l != -INFINITY);
+    live |= ((bal >> gbase) & ((LPR == 64) ? ~0ull : ((1ull << LPR) - 1))) << (k * LPR);
   }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   // In place (output aliases part 0): a row where every other part is empty
   // keeps its values, so it is neither read nor written.
-  if (args.inplace && live == 0) return;
+  if (args.inplace && (live & ~1ull) == 0) return;
+  // Pass 2: live parts PB at a time, their loads issued together (one
+  // dependent load per part would leave the row latency-bound); empty parts
+  // have weight 0 and their O is not read.
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float tot = 0.f;
-  if (m != -INFINITY) {
-    for (int j = 0; j < args.nparts; ++j) {
-      const float l = args.lse[j][li];
-      if (l == -INFINITY) continue;              // weight 0: O_j is not read
-      const float wj = __expf(l - m);
-      const float4 v = *reinterpret_cast<const float4*>(args.o[j] + oi);
-      tot += wj;
-      acc.x += wj * v.x; acc.y += wj * v.y; acc.z += wj * v.z; acc.w += wj * v.w;
+  constexpr int PB = 8;
+  while (live) {
+    int idx[PB];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      idx[u] = live ? __builtin_ctzll(live) : -1;
+      live &= live ? live - 1 : 0ull;
+    }
+    float l[PB];
+    float4 v[PB];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      if (idx[u] >= 0) {
+        l[u] = args.lse[idx[u]][li];
+        v[u] = *reinterpret_cast<const float4*>(args.o[idx[u]] + oi);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      if (idx[u] >= 0) {
+        const float wj = __expf(l[u] - m);
+        tot += wj;
+        acc.x += wj * v[u].x; acc.y += wj * v[u].y; acc.z += wj * v[u].z; acc.w += wj * v[u].w;
+      }
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   OT* dst = reinterpret_cast<OT*>(args.o_out) + oi;
-  dst[0] = static_cast<OT>(acc.x * inv);
-  dst[1] = static_cast<OT>(acc.y * inv);
-  dst[2] = static_cast<OT>(acc.z * inv);
-  dst[3] = static_cast<OT>(acc.w * inv);
+  if constexpr (sizeof(OT) == 2) {
+    bf16x4 pk;
+    pk[0] = static_cast<bf16>(acc.x * inv); pk[1] = static_cast<bf16>(acc.y * inv);
+    pk[2] = static_cast<bf16>(acc.z * inv); pk[3] = static_cast<bf16>(acc.w * inv);
+    *reinterpret_cast<bf16x4*>(dst) = pk;
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
   if (part == 0) args.lse_out[li] = tot > 0.f ? m + __logf(tot) : -INFINITY;
 }
 
