@@ -149,3 +149,35 @@ def test_merge_kernel_edge_cases():
     so, sl = M.merge_partials([o[2]], [lse[2]], torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(so, o[2]) or np.max(np.abs(to_f64(so) - oh[2])) <= 1e-6
+
+
+@pytest.mark.parametrize("d,nparts", [(128, 45), (64, 64), (64, 17), (128, 33)])
+def test_merge_kernel_many_parts(d, nparts):
+    """More partials than a row has lanes (the LSE pass reads several per lane),
+    empty rows in some parts and in all parts, up to the 64-part limit."""
+    require_gpu()
+    announce(f"merge d={d} parts={nparts}")
+    g = torch.Generator(device="cuda").manual_seed(11 + nparts)
+    b, T, H = 1, 53, 5
+    o = [torch.randn((b, T, H, d), generator=g, device="cuda") for _ in range(nparts)]
+    lse = [4.0 * torch.randn((b, H, T), generator=g, device="cuda") for _ in range(nparts)]
+    for j in range(nparts):
+        lse[j][:, :, (j % 7)::7] = -float("inf")
+        o[j][:, (j % 7)::7] = float("nan")        # never read: weight 0
+    for x in lse:
+        x[:, :, 50:] = -float("inf")               # rows empty in every part
+    for x in o:
+        x[:, 50:] = 0.0
+    oh = [np.nan_to_num(to_f64(x)) for x in o]
+    lh = [to_f64(x) for x in lse]
+    ref_o, ref_l = O.merge_partials(oh, lh)
+    for out_dt in (torch.float32, torch.bfloat16):
+        mo, ml = M.merge_partials(o, lse, out_dt)
+        torch.cuda.synchronize()
+        mo_h, ml_h = to_f64(mo), to_f64(ml)
+        assert np.isfinite(mo_h).all()
+        tol = 1e-5 if out_dt == torch.float32 else 2e-2
+        assert np.max(np.abs(mo_h - ref_o)) <= tol
+        fin = np.isfinite(ref_l)
+        assert (np.isneginf(ml_h) == ~fin).all()
+        assert np.max(np.abs(ml_h[fin] - ref_l[fin])) <= 1e-5
