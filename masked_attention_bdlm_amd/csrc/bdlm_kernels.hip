@@ -236,13 +236,21 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
       }
     }
     mx = fmaxf(mx, wave_swap32(mx));
+    // Lazy rescaling: O and l stay relative to the reference m_run until some
+    // row's max exceeds it by more than 8 (log2 units); the exponentials are
+    // then at most 2^8, harmless for fp32 sums and bf16 operands, and the
+    // final O = acc / l and LSE = m_run + log2 l are unchanged.  The rescale
+    // is skipped for the whole wave when no row needs it.
     const float m_new = fmaxf(m_run, mx * args.scale_log2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
+    const bool grow = m_new > m_run + 8.f;
+    if (__ballot(grow)) {
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;   // 0 while m_run = -inf
+      if (grow) m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
     float pv[N / 32][16];
 #pragma unroll
