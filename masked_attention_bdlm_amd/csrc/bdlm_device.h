@@ -202,6 +202,40 @@ template <> __device__ inline float ld_frag_kcrow_s<float, 64>(const float* tile
   return tile[Swz<float, 64>::idx(row0 + c_row(ci, lane >> 5), col0 + (lane & 31))];
 }
 
+// ---- bf16 fragment reads at precomputed per-lane byte offsets
+//
+// On a swizzled bf16 tile the lane-dependent part of a fragment address
+// repeats every 16 rows, so it can be computed once per kernel; the 32-row
+// sub-tile, the 16-row chunk and the buffer go in the instruction's
+// immediate offset or one add per tile.
+//   offA[c]            row-fragment read: row lane%32, k = 16c + 8(lane/32) .. +7
+//   offT[2 dt + h]     transpose read h of ld_frag_kcrow_s(tile, 0, 0, lane, 32 dt)
+template <int D>
+__device__ inline void bf16_frag_offsets(int lane, uint32_t* offA, uint32_t* offT) {
+  using S = Swz<bf16, D>;
+  const int ln = lane & 31, hh = lane >> 5, i16 = lane & 15;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) offA[c] = 2u * (uint32_t)S::idx(ln, (2 * c + hh) * 8);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int r = 4 * hh + 8 * h2 + (i16 >> 2);
+      const int col = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+      offT[2 * dt + h2] = 2u * (uint32_t)S::idx(r, col);
+    }
+  }
+}
+// Row fragment: rows r0 + lane%32 (r0 a multiple of 16) of the tile at `tile`.
+__device__ __forceinline__ bf16x8 ld_fragA(const char* tile, uint32_t off, int r0_bytes) {
+  return *reinterpret_cast<const bf16x8*>(tile + off + r0_bytes);
+}
+// ld_frag_kcrow_s(tile, row0, ci, lane, 32 dt) with row0 + 16 ci in bytes.
+__device__ __forceinline__ bf16x8 ld_fragT(const char* tile, const uint32_t* offT, int dt, int r_bytes) {
+  return cat44(__builtin_bit_cast(bf16x4, ds_read_tr16(tile + offT[2 * dt] + r_bytes)),
+               __builtin_bit_cast(bf16x4, ds_read_tr16(tile + offT[2 * dt + 1] + r_bytes)));
+}
+
 // Global -> LDS DMA of rows [k0, k0+NR) of a [rows, heads, D] array (row
 // stride rs elements, pointer at the head) into a swizzled tile.  Wave `wave`
 // of NW issues every NW-th 1 KB block; each lane moves one 16-byte chunk.

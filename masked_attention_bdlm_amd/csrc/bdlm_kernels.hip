@@ -169,6 +169,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
     dma_rows<T, N, D>(kv_lds[0][1], vb[a0], rs, klo[a0], khi[a0], w, lane);
   }
 
+  // bf16: per-lane fragment offsets, computed once (see bf16_frag_offsets)
+  constexpr bool OFFS = sizeof(T) == 2;
+  uint32_t offA[OFFS ? D / 16 : 1], offT[OFFS ? D / 16 : 1];
+  if constexpr (OFFS) bf16_frag_offsets<D>(lane, offA, offT);
+
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -192,7 +197,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
       constexpr int NB = (N / 32) * (DCH / BT);       // batches over (sub, chunk)
       Frag ka[2][BT];
 #pragma unroll
-      for (int c = 0; c < BT; ++c) ka[0][c] = ld_frag_s<T, D>(k_lds, ln, c * KC + hh * KPL);
+      for (int c = 0; c < BT; ++c) {
+        if constexpr (OFFS) ka[0][c] = ld_fragA(reinterpret_cast<const char*>(k_lds), offA[c], 0);
+        else ka[0][c] = ld_frag_s<T, D>(k_lds, ln, c * KC + hh * KPL);
+      }
 #pragma unroll
       for (int sub = 0; sub < N / 32; ++sub) sacc[sub] = f32x16{};
 #pragma unroll
@@ -200,8 +208,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
         if (nb + 1 < NB) {
           const int sub2 = (nb + 1) / (DCH / BT), cb2 = (nb + 1) % (DCH / BT);
 #pragma unroll
-          for (int c = 0; c < BT; ++c)
-            ka[(nb + 1) & 1][c] = ld_frag_s<T, D>(k_lds, sub2 * 32 + ln, (cb2 * BT + c) * KC + hh * KPL);
+          for (int c = 0; c < BT; ++c) {
+            if constexpr (OFFS)
+              ka[(nb + 1) & 1][c] = ld_fragA(reinterpret_cast<const char*>(k_lds), offA[OFFS ? cb2 * BT + c : 0],
+                                             sub2 * 32 * D * 2);
+            else
+              ka[(nb + 1) & 1][c] = ld_frag_s<T, D>(k_lds, sub2 * 32 + ln, (cb2 * BT + c) * KC + hh * KPL);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         const int sub = nb / (DCH / BT), cb = nb % (DCH / BT);
@@ -271,13 +284,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
     {
       Frag va[2][N / KC];
 #pragma unroll
-      for (int cc = 0; cc < N / KC; ++cc) va[0][cc] = ld_frag_kcrow_s<T, D>(v_lds, (cc / CPS) * 32, cc % CPS, lane, 0);
+      for (int cc = 0; cc < N / KC; ++cc) {
+        if constexpr (OFFS)
+          va[0][cc] = ld_fragT(reinterpret_cast<const char*>(v_lds), offT, 0, ((cc / CPS) * 32 + 16 * (cc % CPS)) * D * 2);
+        else
+          va[0][cc] = ld_frag_kcrow_s<T, D>(v_lds, (cc / CPS) * 32, cc % CPS, lane, 0);
+      }
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         if (dt + 1 < D / 32) {
 #pragma unroll
-          for (int cc = 0; cc < N / KC; ++cc)
-            va[(dt + 1) & 1][cc] = ld_frag_kcrow_s<T, D>(v_lds, (cc / CPS) * 32, cc % CPS, lane, (dt + 1) * 32);
+          for (int cc = 0; cc < N / KC; ++cc) {
+            if constexpr (OFFS)
+              va[(dt + 1) & 1][cc] = ld_fragT(reinterpret_cast<const char*>(v_lds), offT, OFFS ? dt + 1 : 0,
+                                              ((cc / CPS) * 32 + 16 * (cc % CPS)) * D * 2);
+            else
+              va[(dt + 1) & 1][cc] = ld_frag_kcrow_s<T, D>(v_lds, (cc / CPS) * 32, cc % CPS, lane, (dt + 1) * 32);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
