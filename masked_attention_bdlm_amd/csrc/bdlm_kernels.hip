@@ -1056,6 +1056,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  // bf16: per-lane fragment offsets, computed once (see bf16_frag_offsets)
+  constexpr bool OFFS = sizeof(T) == 2;
+  uint32_t offA[OFFS ? D / 16 : 1], offT[OFFS ? D / 16 : 1];
+  if constexpr (OFFS) bf16_frag_offsets<D>(lane, offA, offT);
 
   for (int it = 0; it < total; ++it) {
     const int a = it < nt[0] ? 0 : 1;
@@ -1077,8 +1081,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
         Frag ka[2][BT], va[2][BT];
 #pragma unroll
         for (int c = 0; c < BT; ++c) {
-          ka[0][c] = ld_frag_s<T, D>(k_lds, sub * 32 + ln, c * KC + hh * KPL);
-          va[0][c] = ld_frag_s<T, D>(v_lds, sub * 32 + ln, c * KC + hh * KPL);
+          if constexpr (OFFS) {
+            ka[0][c] = ld_fragA(reinterpret_cast<const char*>(k_lds), offA[c], sub * 32 * D * 2);
+            va[0][c] = ld_fragA(reinterpret_cast<const char*>(v_lds), offA[c], sub * 32 * D * 2);
+          } else {
+            ka[0][c] = ld_frag_s<T, D>(k_lds, sub * 32 + ln, c * KC + hh * KPL);
+            va[0][c] = ld_frag_s<T, D>(v_lds, sub * 32 + ln, c * KC + hh * KPL);
+          }
         }
 #pragma unroll
         for (int cb = 0; cb < DCH / BT; ++cb) {
@@ -1086,8 +1095,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
 #pragma unroll
             for (int c = 0; c < BT; ++c) {
               const int cc = (cb + 1) * BT + c;
-              ka[(cb + 1) & 1][c] = ld_frag_s<T, D>(k_lds, sub * 32 + ln, cc * KC + hh * KPL);
-              va[(cb + 1) & 1][c] = ld_frag_s<T, D>(v_lds, sub * 32 + ln, cc * KC + hh * KPL);
+              if constexpr (OFFS) {
+                ka[(cb + 1) & 1][c] = ld_fragA(reinterpret_cast<const char*>(k_lds), offA[OFFS ? cc : 0], sub * 32 * D * 2);
+                va[(cb + 1) & 1][c] = ld_fragA(reinterpret_cast<const char*>(v_lds), offA[OFFS ? cc : 0], sub * 32 * D * 2);
+              } else {
+                ka[(cb + 1) & 1][c] = ld_frag_s<T, D>(k_lds, sub * 32 + ln, cc * KC + hh * KPL);
+                va[(cb + 1) & 1][c] = ld_frag_s<T, D>(v_lds, sub * 32 + ln, cc * KC + hh * KPL);
+              }
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -1128,13 +1142,21 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
       {
         Frag kt[2][CPS];
 #pragma unroll
-        for (int ci = 0; ci < CPS; ++ci) kt[0][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, 0);
+        for (int ci = 0; ci < CPS; ++ci) {
+          if constexpr (OFFS) kt[0][ci] = ld_fragT(reinterpret_cast<const char*>(k_lds), offT, 0, (sub * 32 + 16 * ci) * D * 2);
+          else kt[0][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, 0);
+        }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           if (dt + 1 < D / 32) {
 #pragma unroll
-            for (int ci = 0; ci < CPS; ++ci)
-              kt[(dt + 1) & 1][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, (dt + 1) * 32);
+            for (int ci = 0; ci < CPS; ++ci) {
+              if constexpr (OFFS)
+                kt[(dt + 1) & 1][ci] = ld_fragT(reinterpret_cast<const char*>(k_lds), offT, OFFS ? dt + 1 : 0,
+                                                (sub * 32 + 16 * ci) * D * 2);
+              else
+                kt[(dt + 1) & 1][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, (dt + 1) * 32);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
