@@ -40,8 +40,8 @@ PEAK_HBM_GBS = 8000.0
 # the counters are taken again.
 MEASURED_TRAFFIC = {
     "kernel": "bdlm_dkdv",
-    "sources_sha256": "ea79f824dd86b8d9fe827c90191824bc96a04d7153110bfa557ea13f16eea090",
-    "fetch_kib": 1.46e7, "fetch_scale": 2.0,
+    "sources_sha256": "835b7fb54ab04332eb5ec16e6e2e2f3e21d25413da03fc82e179452e1b5acdf1",
+    "fetch_kib": 9.305e6, "fetch_scale": 2.0,
     "write_kib": 2.622e5, "write_scale": 1.0,
 }
 KERNEL_SOURCES = ["bdlm_kernels.hip", "bdlm_kernels.h", "bdlm_device.h", "bdlm_common.h"]
