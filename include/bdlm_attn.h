@@ -86,6 +86,12 @@ typedef struct {
   int32_t kv_begin, kv_end;   /* clean-key window [kv_begin, kv_end) of this call,
                                  0 <= kv_begin <= kv_end <= L                       */
   int32_t own_block;          /* 1 = also attend each block's own corrupted K/V     */
+  /* Share mode only: 1 = the local blocks are CLEAN query blocks (the rank's
+     shard of the clean stream in context-parallel form): block i then sees the
+     clean keys of its own and all earlier blocks, [0, (block_ids[i]+1)*B), cut
+     to the window; own_block must be 0.  0 = corrupted blocks (strict clean
+     prefix).  Must be 0 in full mode.                                           */
+  int32_t clean_queries;
 } bdlm_attn_desc;
 
 /* Bytes of scratch memory a call needs (0 is possible).  for_bwd selects
@@ -107,7 +113,12 @@ int bdlm_attn_check_desc(const bdlm_attn_desc* desc);
  *   kc, vc [batch, L, Hkv, d] are the whole clean sequence, of which only rows
  *   [kv_begin, kv_end) are read.  Local block i sees clean keys
  *   [kv_begin, min(kv_end, block_ids[i]*B)) and, if own_block, its own rows
- *   [i*B, (i+1)*B) of kx/vx.  Writes the PARTIAL result over exactly those keys
+ *   [i*B, (i+1)*B) of kx/vx (kx, vx may be NULL when own_block is 0).  With
+ *   clean_queries = 1, qx holds clean query blocks and block i sees clean keys
+ *   [kv_begin, min(kv_end, (block_ids[i]+1)*B)): the clean stream's rule that a
+ *   clean block attends to itself and every earlier clean block (pages: Block
+ *   Parallelism ..., Sec. 4 and Fig. 3, the clean sequence sharded across the
+ *   ranks in context-parallel form).  Writes the PARTIAL result over exactly those keys
  *   to ox (fp32, [batch, n*B, Hq, d]) and lse_x (fp32, [batch, Hq, n*B]); rows
  *   that see no key get O = 0 and LSE = -inf.
  */
@@ -133,7 +144,8 @@ int bdlm_attn_fwd(const bdlm_attn_desc* desc,
  *     - overwrites rows [kv_begin, kv_end) of dkc, dvc ([batch, L, Hkv, d], dtype;
  *       rows no local block sees get 0; other rows are untouched);
  *     - if own_block, overwrites dkx, dvx [batch, n*B, Hkv, d] (dtype); else
- *       dkx, dvx may be NULL and are not touched.
+ *       dkx, dvx (and kx, vx) may be NULL and are not touched.
+ *   clean_queries selects the clean-query rule as in the forward.
  */
 int bdlm_attn_bwd(const bdlm_attn_desc* desc,
                   const void* qc, const void* kc, const void* vc,

@@ -41,7 +41,8 @@ def dtype_code(dt: torch.dtype) -> int:
 
 
 def desc_for(q: torch.Tensor, k: torch.Tensor, block: int, scale: Optional[float] = None,
-             seqlen: Optional[int] = None, block_ids=None, kv_begin=0, kv_end=0, own_block=0):
+             seqlen: Optional[int] = None, block_ids=None, kv_begin=0, kv_end=0, own_block=0,
+             clean_queries=0):
     """Descriptor from Q [batch, tokens, Hq, d] and K [batch, L, Hkv, d]."""
     b, _, hq, d = q.shape
     hkv = k.shape[2]
@@ -49,7 +50,7 @@ def desc_for(q: torch.Tensor, k: torch.Tensor, block: int, scale: Optional[float
     if scale is None:
         scale = d ** -0.5
     return make_desc(b, L, block, hq, hkv, d, dtype_code(q.dtype), scale, block_ids,
-                     kv_begin, kv_end, own_block)
+                     kv_begin, kv_end, own_block, clean_queries)
 
 
 # ---------------------------------------------------------------- C-ABI calls
@@ -121,10 +122,13 @@ def attention_bwd(qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox, block:
 
 
 def share_fwd(qx, kx, vx, kc, vc, block_ids, block: int, kv_begin: int, kv_end: int,
-              own_block: int, scale: Optional[float] = None, out=None, stream=None):
-    """Share-mode partial over one key window: returns (O_part fp32, LSE_part)."""
+              own_block: int, scale: Optional[float] = None, out=None, stream=None, clean_queries: int = 0):
+    """Share-mode partial over one key window: returns (O_part fp32, LSE_part).
+
+    clean_queries=1: qx holds clean query blocks (each sees the clean keys of its
+    own and every earlier block); kx, vx may then be None."""
     desc = desc_for(qx, kc, block, scale, block_ids=block_ids, kv_begin=kv_begin, kv_end=kv_end,
-                    own_block=own_block)
+                    own_block=own_block, clean_queries=clean_queries)
     b, T, hq, d = qx.shape
     if out is None:
         o = torch.empty((b, T, hq, d), dtype=torch.float32, device=qx.device)
@@ -137,10 +141,11 @@ def share_fwd(qx, kx, vx, kc, vc, block_ids, block: int, kv_begin: int, kv_end: 
 
 def share_bwd(qx, kx, vx, kc, vc, block_ids, block: int, kv_begin: int, kv_end: int, own_block: int,
               o_final, lse_final, dox, dqx_acc, dkc, dvc, dkx=None, dvx=None,
-              scale: Optional[float] = None, ws: Optional[torch.Tensor] = None, stream=None):
+              scale: Optional[float] = None, ws: Optional[torch.Tensor] = None, stream=None,
+              clean_queries: int = 0):
     """Share-mode backward of one key window (adds into dqx_acc, writes the window of dkc/dvc)."""
     desc = desc_for(qx, kc, block, scale, block_ids=block_ids, kv_begin=kv_begin, kv_end=kv_end,
-                    own_block=own_block)
+                    own_block=own_block, clean_queries=clean_queries)
     if ws is None:
         ws = workspace(desc, True, qx.device)
     bdlm_attn_bwd(desc, None, kc, vc, qx, kx, vx, None, o_final, None, lse_final, None, dox,

@@ -17,6 +17,13 @@ Chunks that no local block can see (start >= max(block_ids) * B) are skipped.
 Inside a chunk, blocks whose clean prefix ends before the chunk get the empty
 partial (O = 0, LSE = -inf), which the merge kernel recognises without reading
 its O.
+
+The rank's own shard of the clean stream is the context-parallel half of the
+same step (the clean sequence sharded across the ranks, Sec. 4 / Fig. 3 of the
+paper): its clean query blocks attend to the clean keys of their own and every
+earlier block, streamed in the same chunks (clean_share_forward /
+clean_share_backward: the share-mode calls with clean_queries = 1, no
+own-block term).
 """
 from typing import List, Optional, Sequence, Tuple
 
@@ -28,7 +35,7 @@ from .api import bdlm_attn_bwd, bdlm_attn_fwd, bdlm_attn_merge_partials, desc_fo
 class ShareBuffers:
     """Preallocated buffers of a share step (so the timed loop allocates nothing)."""
 
-    def __init__(self, qx: torch.Tensor, kc: torch.Tensor, kx: torch.Tensor):
+    def __init__(self, qx: torch.Tensor, kc: torch.Tensor, kx: Optional[torch.Tensor] = None):
         b, T, hq, d = qx.shape
         dev = qx.device
         self.acc_o = torch.empty((b, T, hq, d), dtype=torch.float32, device=dev)
@@ -40,8 +47,8 @@ class ShareBuffers:
         self.dqx = torch.empty((b, T, hq, d), dtype=torch.float32, device=dev)
         self.dkc = torch.zeros_like(kc)
         self.dvc = torch.zeros_like(kc)
-        self.dkx = torch.empty_like(kx)
-        self.dvx = torch.empty_like(kx)
+        self.dkx = torch.empty_like(kx) if kx is not None else None
+        self.dvx = torch.empty_like(kx) if kx is not None else None
         self.ws = None
 
 
@@ -94,3 +101,57 @@ def share_backward(qx, kx, vx, kc, vc, ids: Sequence[int], B: int, chunk: int, o
     bdlm_attn_bwd(d_own, None, kc, vc, qx, kx, vx, None, o, None, lse, None, dox,
                   None, bufs.dkc, bufs.dvc, bufs.dqx, bufs.dkx, bufs.dvx, bufs.ws, stream)
     return bufs.dqx, bufs.dkc, bufs.dvc, bufs.dkx, bufs.dvx
+
+
+def _clean_chunks(L: int, chunk: int, ids: Sequence[int], B: int) -> List[Tuple[int, int]]:
+    """Chunks that at least one local clean block sees (its prefix includes itself)."""
+    top = (max(ids) + 1) * B
+    return [(j, min(j + chunk, L)) for j in range(0, min(L, top), chunk)]
+
+
+def clean_share_forward(qs, kc, vc, ids: Sequence[int], B: int, chunk: int,
+                        scale: Optional[float] = None, bufs: Optional[ShareBuffers] = None, stream=None):
+    """Final (O, LSE) of the rank's clean query blocks qs [1, n*B, Hq, d] (global
+    clean block ids `ids`) over the clean keys of their own and every earlier
+    block, assembled from streamed chunk partials."""
+    if qs.shape[0] != 1:
+        raise ValueError("the share step streams one sequence (batch 1)")
+    ids = [int(i) for i in ids]
+    L = kc.shape[1]
+    bufs = bufs or ShareBuffers(qs, kc)
+    chunks = _clean_chunks(L, chunk, ids, B)
+    for n, (j0, j1) in enumerate(chunks):
+        d = desc_for(qs, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=j0, kv_end=j1, own_block=0,
+                     clean_queries=1)
+        if n == 0:
+            bdlm_attn_fwd(d, None, kc, vc, qs, None, None, None, bufs.acc_o, None, bufs.acc_lse, None, stream)
+            continue
+        bdlm_attn_fwd(d, None, kc, vc, qs, None, None, None, bufs.part_o, None, bufs.part_lse, None, stream)
+        bdlm_attn_merge_partials([bufs.acc_o, bufs.part_o], [bufs.acc_lse, bufs.part_lse],
+                                 bufs.acc_o, bufs.acc_lse, stream)
+    bdlm_attn_merge_partials([bufs.acc_o], [bufs.acc_lse], bufs.o, bufs.lse, stream)
+    return bufs.o, bufs.lse
+
+
+def clean_share_backward(qs, kc, vc, ids: Sequence[int], B: int, chunk: int, o, lse, dos,
+                         scale: Optional[float] = None, bufs: Optional[ShareBuffers] = None, stream=None):
+    """Gradients of the clean-query share: returns (dq fp32, dkc, dvc).  dkc/dvc
+    rows that no local block sees are zero."""
+    ids = [int(i) for i in ids]
+    L = kc.shape[1]
+    bufs = bufs or ShareBuffers(qs, kc)
+    bufs.dqx.zero_()
+    top = (max(ids) + 1) * B
+    if top < L:
+        bufs.dkc[:, top:].zero_()
+        bufs.dvc[:, top:].zero_()
+    d_full = desc_for(qs, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=0, kv_end=L, own_block=0,
+                      clean_queries=1)
+    if bufs.ws is None:
+        bufs.ws = workspace(d_full, True, qs.device)
+    for (j0, j1) in _clean_chunks(L, chunk, ids, B):
+        d = desc_for(qs, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=j0, kv_end=j1, own_block=0,
+                     clean_queries=1)
+        bdlm_attn_bwd(d, None, kc, vc, qs, None, None, None, o, None, lse, None, dos,
+                      None, bufs.dkc, bufs.dvc, bufs.dqx, None, None, bufs.ws, stream)
+    return bufs.dqx, bufs.dkc, bufs.dvc

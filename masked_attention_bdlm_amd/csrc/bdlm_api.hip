@@ -72,6 +72,10 @@ int check_desc(const bdlm_attn_desc* d) {
     }
     if (d->kv_begin < 0 || d->kv_begin > d->kv_end || d->kv_end > d->seqlen) return BDLM_ERR_INVALID_ARG;
     if (d->own_block != 0 && d->own_block != 1) return BDLM_ERR_INVALID_ARG;
+    if (d->clean_queries != 0 && d->clean_queries != 1) return BDLM_ERR_INVALID_ARG;
+    if (d->clean_queries && d->own_block) return BDLM_ERR_INVALID_ARG;
+  } else if (d->clean_queries != 0) {
+    return BDLM_ERR_INVALID_ARG;
   }
   return BDLM_OK;
 }
@@ -95,6 +99,7 @@ Problem make_problem(const bdlm_attn_desc* d) {
     p.rows[0] = 0; p.rows[1] = p.nlocal * p.B;
     p.klen[0] = p.L; p.klen[1] = p.nlocal * p.B;
     p.kv_begin = d->kv_begin; p.kv_end = d->kv_end; p.own_block = d->own_block;
+    p.incl = d->clean_queries;
     for (int i = 0; i < p.nlocal; ++i) p.block_ids[i] = d->block_ids[i];
   }
   return p;
@@ -150,7 +155,7 @@ const char* bdlm_status_str(int s) {
   }
 }
 
-int bdlm_attn_version(void) { return 100; }
+int bdlm_attn_version(void) { return 110; }
 
 int bdlm_attn_check_desc(const bdlm_attn_desc* desc) { return check_desc(desc); }
 
@@ -169,6 +174,8 @@ int bdlm_attn_fwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   const bool share = desc->num_local_blocks > 0;
   if (share) {
     if (qc || oc || lse_c) return BDLM_ERR_INVALID_ARG;
+    // without own_block no local K/V is read: NULL kx/vx stand in as kc/vc
+    if (!desc->own_block && !kx && !vx) { kx = kc; vx = vc; }
   } else {
     if (!qc || !oc || !lse_c || !aligned16(qc) || !aligned16(oc) || !aligned4(lse_c)) return BDLM_ERR_INVALID_ARG;
   }
@@ -211,6 +218,8 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
     if (qc || oc || lse_c || doc || dqc) return BDLM_ERR_INVALID_ARG;
     if (desc->own_block) {
       if (!dkx || !dvx || !aligned16(dkx) || !aligned16(dvx)) return BDLM_ERR_INVALID_ARG;
+    } else if (!kx && !vx) {
+      kx = kc; vx = vc;   // never read without own_block
     }
   } else {
     const void* need[] = {qc, oc, doc, dqc, dkx, dvx};

@@ -29,6 +29,7 @@ struct Problem {
   int rows[2];        // query rows per stream array: full {L, L}; share {0, n*B}
   int klen[2];        // key rows per key array:      full {L, L}; share {L, n*B}
   int kv_begin, kv_end, own_block;
+  int incl;           // share mode: 1 = local blocks are clean queries (prefix includes the block)
   int nlocal;
   int block_ids[kMaxLocalBlocks];
 };
@@ -59,9 +60,9 @@ __host__ __device__ inline void row_keys(const Problem& p, int s, int r, int a, 
     }
   } else {
     const int i = div_b(p, r);   // local block index
-    if (a == 0) {            // clean window cut to the block's strict clean prefix
-      lo = p.kv_begin;
-      int e = p.block_ids[i] * p.B;
+    if (a == 0) {            // clean window cut to the block's clean prefix
+      lo = p.kv_begin;       // (strict for corrupted blocks, inclusive for clean ones)
+      int e = (p.block_ids[i] + p.incl) * p.B;
       hi = e < p.kv_end ? e : p.kv_end;
       if (hi < lo) hi = lo;
     } else if (p.own_block) {

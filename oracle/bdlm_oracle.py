@@ -244,37 +244,44 @@ def merge_partials(o_parts, lse_parts):
 
 
 # --------------------------------------------------------------- CSBP share partials
-def share_keys(block_id, block, local_index, kv_begin, kv_end, own_block):
-    """Key sets of local corrupted block `local_index` (global id `block_id`) in
-    one share-mode call: clean tokens [kv_begin, kv_end) cut to the block's
-    strict clean prefix [0, block_id*B), and its own corrupted rows
-    [local_index*B, (local_index+1)*B) of the local arrays when own_block."""
+def share_keys(block_id, block, local_index, kv_begin, kv_end, own_block, clean_queries=False):
+    """Key sets of local block `local_index` (global id `block_id`) in one
+    share-mode call: clean tokens [kv_begin, kv_end) cut to the block's clean
+    prefix, and its own corrupted rows [local_index*B, (local_index+1)*B) of the
+    local arrays when own_block.  The prefix is the mask's: a corrupted block
+    sees the clean blocks before it, [0, block_id*B); a clean block (the clean
+    stream in context-parallel form, clean_queries) sees the clean blocks up to
+    and including itself, [0, (block_id+1)*B), and no corrupted keys."""
     c_lo = max(kv_begin, 0)
-    c_hi = min(kv_end, block_id * block)
+    c_hi = min(kv_end, (block_id + (1 if clean_queries else 0)) * block)
     clean = np.arange(c_lo, c_hi) if c_hi > c_lo else np.arange(0)
     own = (np.arange(local_index * block, (local_index + 1) * block) if own_block
            else np.arange(0))
     return clean, own
 
 
-def share_fwd(qx, kx, vx, kc, vc, block_ids, block, kv_begin, kv_end, own_block, scale):
-    """Partial (O, LSE) of a rank's local corrupted blocks over one key chunk.
+def share_fwd(qx, kx, vx, kc, vc, block_ids, block, kv_begin, kv_end, own_block, scale,
+              clean_queries=False):
+    """Partial (O, LSE) of a rank's local blocks over one key chunk.
 
     qx/kx/vx [batch, nlocal*B, H, d] are the local blocks in id order; kc/vc
-    [batch, L, Hkv, d] the clean sequence.  Returns O [batch, nlocal*B, Hq, d]
-    and LSE [batch, Hq, nlocal*B]; rows without a visible key get (0, -inf)."""
+    [batch, L, Hkv, d] the clean sequence (kx/vx are unused, may be None, for
+    clean query blocks).  Returns O [batch, nlocal*B, Hq, d] and LSE
+    [batch, Hq, nlocal*B]; rows without a visible key get (0, -inf)."""
     bsz, T, hq, d = qx.shape
     hkv = kc.shape[2]
     o = np.zeros((bsz, T, hq, d))
     lse = np.full((bsz, hq, T), -np.inf)
     for i, bid in enumerate(block_ids):
         r = slice(i * block, (i + 1) * block)
-        ci, xi = share_keys(int(bid), block, i, kv_begin, kv_end, own_block)
+        ci, xi = share_keys(int(bid), block, i, kv_begin, kv_end, own_block, clean_queries)
         for b in range(bsz):
             for h in range(hq):
                 g = kv_head_of(h, hq, hkv)
-                keys = np.concatenate([kc[b, ci, g], kx[b, xi, g]], axis=0)
-                vals = np.concatenate([vc[b, ci, g], vx[b, xi, g]], axis=0)
+                keys, vals = kc[b, ci, g], vc[b, ci, g]
+                if len(xi):
+                    keys = np.concatenate([keys, kx[b, xi, g]], axis=0)
+                    vals = np.concatenate([vals, vx[b, xi, g]], axis=0)
                 full = np.ones((block, keys.shape[0]), dtype=bool)
                 oh, lh, _ = attention_fwd(qx[b, r, h], keys, vals, full, scale)
                 o[b, r, h] = oh
@@ -283,7 +290,7 @@ def share_fwd(qx, kx, vx, kc, vc, block_ids, block, kv_begin, kv_end, own_block,
 
 
 def share_bwd(qx, kx, vx, kc, vc, block_ids, block, kv_begin, kv_end, own_block,
-              o_final, lse_final, dox, scale):
+              o_final, lse_final, dox, scale, clean_queries=False):
     """Backward of one share-mode key chunk with the final (merged) O and LSE.
 
     P = exp(S - LSE_final) on the chunk's keys, D = rowsum(dO * O_final)
@@ -300,15 +307,17 @@ def share_bwd(qx, kx, vx, kc, vc, block_ids, block, kv_begin, kv_end, own_block,
     dvx = np.zeros_like(dkx)
     for i, bid in enumerate(block_ids):
         r = slice(i * block, (i + 1) * block)
-        ci, xi = share_keys(int(bid), block, i, kv_begin, kv_end, own_block)
+        ci, xi = share_keys(int(bid), block, i, kv_begin, kv_end, own_block, clean_queries)
         nc = len(ci)
         if nc + len(xi) == 0:
             continue
         for b in range(bsz):
             for h in range(hq):
                 g = kv_head_of(h, hq, hkv)
-                keys = np.concatenate([kc[b, ci, g], kx[b, xi, g]], axis=0)
-                vals = np.concatenate([vc[b, ci, g], vx[b, xi, g]], axis=0)
+                keys, vals = kc[b, ci, g], vc[b, ci, g]
+                if len(xi):
+                    keys = np.concatenate([keys, kx[b, xi, g]], axis=0)
+                    vals = np.concatenate([vals, vx[b, xi, g]], axis=0)
                 s = scale * (qx[b, r, h] @ keys.T)
                 p = np.exp(s - lse_final[b, h, r][:, None])
                 delta = (dox[b, r, h] * o_final[b, r, h]).sum(axis=1)

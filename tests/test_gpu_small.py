@@ -102,6 +102,37 @@ def test_share_mode_chunked_merge_and_backward(dtype, L, B, n, chunk, sharp):
     check_outputs(got, ref, dtype, where="share")
 
 
+@pytest.mark.parametrize("dtype,L,B,n,chunk,sharp", [
+    ("bf16", 2048, 128, 4, 512, False),
+    ("bf16", 1024, 64, 5, 384, True),       # chunks not aligned to blocks
+    ("f32", 1024, 64, 3, 320, False),
+])
+def test_clean_query_share_chunked_merge_and_backward(dtype, L, B, n, chunk, sharp):
+    """The rank's clean query blocks (clean_queries = 1: own and earlier clean
+    blocks visible, no corrupted keys) streamed over clean chunks with the
+    running merge, then the chunked backward, against the oracle's one pass."""
+    from masked_attention_bdlm_amd import csbp
+    require_gpu()
+    w = Workload(name="clean_share_small", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=128,
+                 dtype=dtype, seed=13, q_std=128 ** -0.5, share_blocks=n, share_chunk=chunk)
+    announce(f"clean-query share {dtype} L={L} B={B} n={n} chunk={chunk} sharp={sharp}")
+    x = make_share_inputs(w, device="cuda", sharp=sharp)
+    ids = [int(i) for i in x["block_ids"]]
+    bufs = csbp.ShareBuffers(x["qx"], x["kc"])
+    o, lse = csbp.clean_share_forward(x["qx"], x["kc"], x["vc"], ids, B, chunk, w.scale, bufs)
+    dq, dkc, dvc = csbp.clean_share_backward(x["qx"], x["kc"], x["vc"], ids, B, chunk, o, lse, x["dox"],
+                                             w.scale, bufs)
+    torch.cuda.synchronize()
+    got = host(dict(ox=o, lse_x=lse, dqx=dq, dkc=dkc, dvc=dvc))
+    xh = host(x)
+    o_ref, lse_ref = O.share_fwd(xh["qx"], None, None, xh["kc"], xh["vc"], ids, B, 0, L, 0, w.scale,
+                                 clean_queries=True)
+    r = O.share_bwd(xh["qx"], None, None, xh["kc"], xh["vc"], ids, B, 0, L, 0, o_ref, lse_ref, xh["dox"],
+                    w.scale, clean_queries=True)
+    ref = dict(ox=o_ref, lse_x=lse_ref, dqx=r[0], dkc=r[1], dvc=r[2])
+    check_outputs(got, ref, dtype, where="clean-query share")
+
+
 def test_share_partial_of_empty_window_is_minus_inf():
     require_gpu()
     w = Workload(name="share_empty", batch=1, seqlen=1024, block=64, hq=2, hkv=1, head_dim=64,

@@ -42,7 +42,8 @@ def _ok_desc(**kw):
     base.update(kw)
     return make_desc(base["batch"], base["seqlen"], base["block"], base["hq"], base["hkv"],
                      base["head_dim"], base["dtype"], base["scale"], base.get("block_ids"),
-                     base.get("kv_begin", 0), base.get("kv_end", 0), base.get("own_block", 0))
+                     base.get("kv_begin", 0), base.get("kv_end", 0), base.get("own_block", 0),
+                     base.get("clean_queries", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -63,6 +64,10 @@ def _ok_desc(**kw):
     ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 300}, 1),
     ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "own_block": 2}, 1),
     ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "own_block": 1}, 0),
+    ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "clean_queries": 1}, 0),
+    ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "clean_queries": 1, "own_block": 1}, 1),
+    ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "clean_queries": 2}, 1),
+    ({"clean_queries": 1}, 1),       # clean-query rule needs share mode
     ({"seqlen": 8192, "block": 16, "block_ids": list(range(300)), "kv_begin": 0, "kv_end": 16}, 2),
 ])
 def test_descriptor_validation(kw, code):
@@ -159,18 +164,25 @@ SHARE_CASES = [
     (1024, 64, [2, 9, 10, 15], (100, 700), 1),     # unaligned window
     (4096, 1024, [0, 3], (0, 4096), 1),
 ]
+# clean query blocks (own block excluded): the prefix includes the block itself
+CLEAN_SHARE_CASES = [
+    (512, 16, [0, 3, 7, 20, 31], (0, 512), 0),
+    (512, 16, [0, 3, 7, 20, 31], (48, 64), 0),      # window = one block's own keys
+    (1024, 64, [2, 9, 10, 15], (100, 700), 0),      # unaligned window
+    (4096, 1024, [0, 3], (0, 4096), 0),
+]
 
 
-@pytest.mark.parametrize("L,B,ids,win,own", SHARE_CASES)
+@pytest.mark.parametrize("L,B,ids,win,own,cq", [c + (0,) for c in SHARE_CASES] + [c + (1,) for c in CLEAN_SHARE_CASES])
 @pytest.mark.parametrize("for_bwd", [0, 1, 2])
-def test_share_schedule_covers_exactly_the_key_sets(L, B, ids, win, own, for_bwd):
-    desc = make_desc(1, L, B, 2, 1, 128, 1, 0.1, ids, win[0], win[1], own)
+def test_share_schedule_covers_exactly_the_key_sets(L, B, ids, win, own, cq, for_bwd):
+    desc = make_desc(1, L, B, 2, 1, 128, 1, 0.1, ids, win[0], win[1], own, cq)
     cover, st = M.schedule_walk(desc, for_bwd)
     assert st["errors"] == 0
     n = len(ids)
     expect = np.zeros((n * B, L + n * B), dtype=np.uint8)
     for i, bid in enumerate(ids):
-        clean, mine = O.share_keys(bid, B, i, win[0], win[1], own)
+        clean, mine = O.share_keys(bid, B, i, win[0], win[1], own, bool(cq))
         expect[i * B:(i + 1) * B, clean] = 1
         expect[i * B:(i + 1) * B, L + mine] = 1
     np.testing.assert_array_equal(cover, expect)

@@ -311,6 +311,67 @@ def test_chunked_backward_sums_to_per_block_backward(chunk):
             np.testing.assert_allclose(one[0][0, r, h], qt.grad.numpy(), atol=1e-12)
 
 
+@pytest.mark.parametrize("chunk", [8, 24, 64])
+def test_clean_query_share_equals_full_clean_stream(chunk):
+    """The rank's clean query blocks, streamed over clean chunks and merged,
+    give the full 2L computation's clean-stream rows (forward), and the summed
+    chunk backwards give its dQ rows and its clean dK/dV when only those rows
+    carry an upstream gradient."""
+    L, B, hq, hkv, d = 64, 8, 2, 1, 4
+    rng = np.random.default_rng(70 + chunk)
+    ids = np.sort(rng.choice(L // B, size=3, replace=False))
+    T = len(ids) * B
+    kc, vc = _rand(rng, 1, L, hkv, d), _rand(rng, 1, L, hkv, d)
+    qc_f = _rand(rng, 1, L, hq, d)
+    qx_f, kx_f, vx_f = _rand(rng, 1, L, hq, d), _rand(rng, 1, L, hkv, d), _rand(rng, 1, L, hkv, d)
+    qs = np.concatenate([qc_f[:, b * B:(b + 1) * B] for b in ids], axis=1)
+    dos = _rand(rng, 1, T, hq, d)
+    scale = 0.6
+    wins = [(j, min(j + chunk, L)) for j in range(0, L, chunk)]
+    parts = [O.share_fwd(qs, None, None, kc, vc, ids, B, j, e, 0, scale, clean_queries=True) for j, e in wins]
+    o_m, lse_m = O.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    doc_f = np.zeros_like(qc_f)
+    for i, b in enumerate(ids):
+        doc_f[0, b * B:(b + 1) * B] = dos[0, i * B:(i + 1) * B]
+    full = O.bdlm_fwd_bwd(qc_f, kc, vc, qx_f, kx_f, vx_f, doc_f, np.zeros_like(qx_f), B, scale)
+    for i, b in enumerate(ids):
+        np.testing.assert_allclose(o_m[0, i * B:(i + 1) * B], full["oc"][0, b * B:(b + 1) * B], atol=1e-14)
+        np.testing.assert_allclose(lse_m[0, :, i * B:(i + 1) * B], full["lse_c"][0, :, b * B:(b + 1) * B],
+                                   atol=1e-13)
+    dq = np.zeros_like(qs)
+    dkc = np.zeros_like(kc)
+    dvc = np.zeros_like(vc)
+    for j, e in wins:
+        r = O.share_bwd(qs, None, None, kc, vc, ids, B, j, e, 0, o_m, lse_m, dos, scale, clean_queries=True)
+        dq += r[0]
+        dkc[:, j:e] = r[1]
+        dvc[:, j:e] = r[2]
+        assert not r[3].any() and not r[4].any()
+    for i, b in enumerate(ids):
+        np.testing.assert_allclose(dq[0, i * B:(i + 1) * B], full["dqc"][0, b * B:(b + 1) * B], atol=1e-13)
+    np.testing.assert_allclose(dkc, full["dkc"], atol=1e-13)
+    np.testing.assert_allclose(dvc, full["dvc"], atol=1e-13)
+    assert not full["dkx"].any() and not full["dvx"].any()
+
+
+def test_clean_query_share_block_is_attention_over_its_inclusive_prefix():
+    """Each clean query block of a one-pass clean-query share is plain attention
+    (torch SDPA in fp64) over the clean keys of its own and earlier blocks."""
+    L, B, hq, hkv, d = 48, 8, 2, 1, 4
+    rng = np.random.default_rng(77)
+    ids = np.array([0, 2, 5])
+    kc, vc = _rand(rng, 1, L, hkv, d), _rand(rng, 1, L, hkv, d)
+    qs = _rand(rng, 1, len(ids) * B, hq, d)
+    o, lse = O.share_fwd(qs, None, None, kc, vc, ids, B, 0, L, 0, 0.7, clean_queries=True)
+    for i, b in enumerate(ids):
+        r = slice(i * B, (i + 1) * B)
+        for h in range(hq):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.tensor(qs[0, r, h])[None], torch.tensor(kc[0, :(b + 1) * B, 0])[None],
+                torch.tensor(vc[0, :(b + 1) * B, 0])[None], scale=0.7)[0]
+            np.testing.assert_allclose(o[0, r, h], ref.numpy(), atol=1e-14)
+
+
 def test_merge_edge_cases():
     rng = np.random.default_rng(20)
     o1, o2 = _rand(rng, 1, 3, 2, 4), _rand(rng, 1, 3, 2, 4)
