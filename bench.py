@@ -152,7 +152,8 @@ def bench_share(args, w, dev, stream):
     kernel alone, HBM-bound)."""
     import torch
     from masked_attention_bdlm_amd.api import bdlm_attn_merge_partials
-    from masked_attention_bdlm_amd.csbp import ShareBuffers, _chunks, share_backward, share_forward
+    from masked_attention_bdlm_amd.csbp import (ShareBuffers, _chunks, _clean_chunks, clean_share_backward,
+                                                clean_share_forward, share_backward, share_forward)
     from synth import make_share_inputs
 
     x = make_share_inputs(w, device=dev)
@@ -161,6 +162,10 @@ def bench_share(args, w, dev, stream):
     T = len(ids) * B
     log(f"workload {w.name}: {len(ids)} local blocks of {B} at ids {ids}, clean L {L}, chunk {w.share_chunk}")
     bufs = ShareBuffers(x["qx"], x["kc"], x["kx"])
+    cids = [int(i) for i in x["clean_ids"]] if w.clean_share else []
+    if cids:
+        log(f"clean query shard (rank 0 of {w.share_ranks}, zigzag): blocks {cids}")
+        cbufs = ShareBuffers(x["qs"], x["kc"])
     torch.cuda.synchronize()
 
     def step():
@@ -168,10 +173,19 @@ def bench_share(args, w, dev, stream):
                                w.scale, bufs, stream)
         share_backward(x["qx"], x["kx"], x["vx"], x["kc"], x["vc"], ids, B, w.share_chunk, o, lse,
                        x["dox"], w.scale, bufs, stream)
+        if cids:
+            oc, lc = clean_share_forward(x["qs"], x["kc"], x["vc"], cids, B, w.share_chunk, w.scale, cbufs,
+                                         stream)
+            clean_share_backward(x["qs"], x["kc"], x["vc"], cids, B, w.share_chunk, oc, lc, x["dos"], w.scale,
+                                 cbufs, stream)
 
     nchunks = len(_chunks(L, w.share_chunk, ids, B))
-    ms, per_step, kt = time_steps(step, args.steps, args.warmup, launches_per_step=8 * nchunks + 16)
-    pairs = sum(B * B * (bid + 1) for bid in ids)        # clean prefix b_i*B plus the own block
+    ncchunks = len(_clean_chunks(L, w.share_chunk, cids, B)) if cids else 0
+    ms, per_step, kt = time_steps(step, args.steps, args.warmup,
+                                  launches_per_step=8 * (nchunks + ncchunks) + 24)
+    # visible pairs: corrupted block b_i sees its clean prefix b_i*B plus its own
+    # block; clean block c_j sees the clean blocks up to and including itself
+    pairs = sum(B * B * (bid + 1) for bid in ids) + sum(B * B * (c + 1) for c in cids)
     useful = 14.0 * d * pairs * hq
     kernels = {k: {"launches": n, "avg_ms": tt / max(n, 1), "total_ms": tt} for k, (n, tt) in kt.times.items()}
 
@@ -195,8 +209,10 @@ def bench_share(args, w, dev, stream):
     mms = e0.elapsed_time(e1) / reps
     mbytes = T * hq * (nparts * (4 * d + 4) + (mo.element_size() * d + 4))
     out = {
-        "metric": "BDLM attn CSBP share (one rank's corrupted blocks vs the streamed clean prefix) "
-                  "fwd+bwd useful TFLOP/s, 1 GPU",
+        "metric": ("BDLM attn CSBP rank share (corrupted blocks and the clean query shard vs the streamed "
+                   "clean prefix) fwd+bwd useful TFLOP/s, 1 GPU" if cids else
+                   "BDLM attn CSBP share (one rank's corrupted blocks vs the streamed clean prefix) "
+                   "fwd+bwd useful TFLOP/s, 1 GPU"),
         "value": round(useful / (ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -204,7 +220,9 @@ def bench_share(args, w, dev, stream):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "clean_len": L, "block": B, "local_blocks": len(ids),
-                   "block_ids": ids, "chunk": w.share_chunk, "chunks": nchunks, "q_heads": hq,
+                   "block_ids": ids, "chunk": w.share_chunk, "chunks": nchunks,
+                   **({"clean_block_ids": cids, "clean_chunks": ncchunks, "ranks": w.share_ranks} if cids else {}),
+                   "q_heads": hq,
                    "kv_heads": w.hkv, "head_dim": d, "parallelism": "single GPU (one rank's share)"},
         "pct_of_peak": round(100.0 * useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "useful_flop_per_step": useful,

@@ -9,6 +9,7 @@ from .inputs import (  # noqa: F401
     draw_normal,
     make_full_inputs,
     make_share_inputs,
+    clean_shard_ids,
     draw_block_positions,
     draw_units,
     to_f64,

@@ -121,7 +121,27 @@ def make_share_inputs(w, device="cpu", sharp: bool = False, seqlen: Optional[int
     for k in list(out):
         out[k] = out[k].to(td).contiguous()
     out["block_ids"] = draw_block_positions(L // B, nl, s)
+    if w.clean_share:
+        ids = clean_shard_ids(L // B, w.share_ranks, 0)
+        Tc = len(ids) * B
+        out["qs"] = draw_normal((1, Tc, w.hq, w.head_dim), s, 8, device, qk_std).to(td).contiguous()
+        out["dos"] = draw_normal((1, Tc, w.hq, w.head_dim), s, 9, device, 1.0).to(td).contiguous()
+        out["clean_ids"] = ids
     return out
+
+
+def clean_shard_ids(nblocks: int, nranks: int, rank: int) -> np.ndarray:
+    """Clean blocks of `rank` when the clean sequence is sharded over `nranks`
+    ranks in the zigzag layout: the blocks are cut into 2*nranks equal runs and
+    rank r takes runs r and 2*nranks-1-r, which gives every rank the same
+    number of visible (query, key) pairs under the clean stream's block-causal
+    rule (a block b sees b+1 blocks).  Sorted block ids."""
+    if nblocks % (2 * nranks):
+        raise ValueError("nblocks must be a multiple of 2*nranks")
+    run = nblocks // (2 * nranks)
+    a = np.arange(rank * run, (rank + 1) * run)
+    b = np.arange((2 * nranks - 1 - rank) * run, (2 * nranks - rank) * run)
+    return np.concatenate([a, b]).astype(np.int64)
 
 
 def draw_units(nblocks: int, hq: int, batch: int, count: int, seed: int,

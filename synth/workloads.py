@@ -27,6 +27,8 @@ class Workload:
     # CSBP share mode (one rank's corrupted blocks against a streamed clean prefix)
     share_blocks: int = 0       # number of local corrupted blocks (0 = full mode)
     share_chunk: int = 0        # clean tokens per streamed chunk
+    clean_share: bool = False   # also the rank's own clean query shard (context-parallel half)
+    share_ranks: int = 16       # ranks the clean sequence is sharded over
     units: int = 64             # sampled (batch, stream, block, head) units for the oracle
     note: str = ""
 
@@ -67,6 +69,13 @@ WORKLOADS = {
     "csbp_share_256k": _w(name="csbp_share_256k", batch=1, seqlen=262144, block=1024,
                           hq=32, hkv=8, head_dim=128, dtype="bf16", seed=4,
                           q_std=1.0 / 128 ** 0.5, share_blocks=16, share_chunk=8192),
+    # The whole attention share of one of 16 ranks at 256K: the corrupted blocks
+    # above plus the rank's zigzag shard of the clean sequence (16 clean blocks
+    # of 1024, query side), both against the streamed clean K/V.
+    "csbp_rank_256k": _w(name="csbp_rank_256k", batch=1, seqlen=262144, block=1024,
+                         hq=32, hkv=8, head_dim=128, dtype="bf16", seed=4,
+                         q_std=1.0 / 128 ** 0.5, share_blocks=16, share_chunk=8192,
+                         clean_share=True, share_ranks=16),
     # Block-size sweep at 2L = 256K.
     "sweep_256k_B128": _w(name="sweep_256k_B128", batch=1, seqlen=131072, block=128, hq=32,
                           hkv=8, head_dim=128, dtype="bf16", seed=5128,

@@ -223,3 +223,65 @@ def test_csbp_share_256k_sampled():
         e = rel_fro(a, ref)
         announce(f"{w.name} dO-masked {name} rel {e:.3e}")
         assert e <= TOL_REL, (name, e)
+
+
+def test_csbp_rank_256k_clean_shard_sampled():
+    """The clean-query half of one rank's share at 256K: the rank's zigzag shard
+    of 16 clean blocks of 1024 against the streamed clean K/V (each block sees
+    its own and every earlier clean block).  Sampled rows of O, LSE and dQ
+    against the oracle's attention over the block's inclusive prefix, and the
+    dO-masked rerun's dK/dV against those rows' contributions."""
+    require_gpu()
+    w = WORKLOADS["csbp_rank_256k"]
+    announce(w.name + " clean shard")
+    x = make_share_inputs(w, device="cuda")
+    ids = [int(i) for i in x["clean_ids"]]
+    B, L = w.block, w.seqlen
+    bufs = csbp.ShareBuffers(x["qs"], x["kc"])
+    o, lse = csbp.clean_share_forward(x["qs"], x["kc"], x["vc"], ids, B, w.share_chunk, w.scale, bufs)
+    o, lse = o.clone(), lse.clone()
+    dq, _, _ = (t.clone() for t in csbp.clean_share_backward(
+        x["qs"], x["kc"], x["vc"], ids, B, w.share_chunk, o, lse, x["dos"], w.scale, bufs))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed + 200)
+    units = [(i, int(rng.integers(w.hq))) for i in (0, len(ids) - 1)]
+    while len(units) < 16:
+        u = (int(rng.integers(len(ids))), int(rng.integers(w.hq)))
+        if u not in units:
+            units.append(u)
+    offs = row_sample(B, 32, w.seed + 9)
+    kc_h, vc_h = HostView(x["kc"]), HostView(x["vc"])
+    gs, rs = {"o": [], "lse": [], "dq": []}, {"o": [], "lse": [], "dq": []}
+    dkc_s = np.zeros((L, w.hkv, w.head_dim))
+    dvc_s = np.zeros_like(dkc_s)
+    dos2 = torch.zeros_like(x["dos"])
+    for (i, h) in units:
+        g = h // (w.hq // w.hkv)
+        cid = ids[i]
+        rows = _rows(offs, i, B, x["qs"].device)
+        keys, vals = kc_h[0, :(cid + 1) * B, g], vc_h[0, :(cid + 1) * B, g]
+        q = to_f64(x["qs"][0, rows, h])
+        do = to_f64(x["dos"][0, rows, h])
+        ro, rl, p = O.attention_fwd(q, keys, vals, np.ones((len(offs), len(keys)), dtype=bool), w.scale)
+        rdq, rdk, rdv = O.attention_bwd(q, keys, vals, p, ro, do, w.scale)
+        del p
+        gs["o"].append(to_f64(o[0, rows, h])); rs["o"].append(ro)
+        gs["lse"].append(to_f64(lse[0, h, rows])); rs["lse"].append(rl)
+        gs["dq"].append(to_f64(dq[0, rows, h])); rs["dq"].append(rdq)
+        dkc_s[:(cid + 1) * B, g] += rdk
+        dvc_s[:(cid + 1) * B, g] += rdv
+        dos2[0, rows, h] = x["dos"][0, rows, h]
+    gg = {k + ("x" if k != "lse" else "_x"): np.concatenate(v) for k, v in gs.items()}
+    rr = {k + ("x" if k != "lse" else "_x"): np.concatenate(v) for k, v in rs.items()}
+    rep = check_outputs(gg, rr, w.dtype, where=w.name)
+    announce(f"{w.name} clean shard sampled rows: {rep}")
+    _, g_dkc, g_dvc = csbp.clean_share_backward(x["qs"], x["kc"], x["vc"], ids, B, w.share_chunk, o, lse, dos2,
+                                                w.scale, bufs)
+    torch.cuda.synchronize()
+    for name, gt, ref in (("dkc", g_dkc, dkc_s), ("dvc", g_dvc, dvc_s)):
+        a = to_f64(gt[0])
+        seen = np.any(ref != 0, axis=-1)
+        assert not np.any(a[~seen]), f"{name}: non-zero gradient on unseen keys"
+        e = rel_fro(a, ref)
+        announce(f"{w.name} clean shard dO-masked {name} rel {e:.3e}")
+        assert e <= TOL_REL, (name, e)

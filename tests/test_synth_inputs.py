@@ -38,3 +38,22 @@ def test_share_inputs():
     x = make_share_inputs(w, seqlen=8192, nlocal=4, block=256)
     assert x["qx"].shape == (1, 1024, 32, 128) and x["kc"].shape == (1, 8192, 8, 128)
     assert len(x["block_ids"]) == 4
+
+
+def test_clean_shard_ids_zigzag_is_balanced_and_partitions():
+    from synth import clean_shard_ids
+    nb, nr = 256, 16
+    shards = [clean_shard_ids(nb, nr, r) for r in range(nr)]
+    allb = np.sort(np.concatenate(shards))
+    np.testing.assert_array_equal(allb, np.arange(nb))        # a partition of the blocks
+    work = [int((s + 1).sum()) for s in shards]                 # block b sees b + 1 clean blocks
+    assert len(set(work)) == 1
+    assert list(shards[0][:3]) == [0, 1, 2] and shards[0][-1] == nb - 1
+
+
+def test_rank_share_inputs_include_the_clean_shard():
+    w = WORKLOADS["csbp_rank_256k"]
+    x = make_share_inputs(w, seqlen=65536, nlocal=4)       # 64 blocks over 16 ranks: 4 each
+    assert x["qs"].shape == (1, 4 * w.block, w.hq, w.head_dim) and x["qs"].dtype == torch.bfloat16
+    assert x["dos"].shape == x["qs"].shape
+    assert list(x["clean_ids"]) == [0, 1, 62, 63]
