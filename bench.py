@@ -237,6 +237,62 @@ def bench_share(args, w, dev, stream):
     print(json.dumps(out), flush=True)
 
 
+def bench_balance(args, w, dev, stream):
+    """Every rank's whole attention share (its corrupted blocks and its clean
+    query shard against the streamed clean K/V) timed one after another on this
+    GPU, for the contiguous and the zigzag block layout: the slowest rank sets
+    the step time of a data-parallel-free CSBP layer, so max/mean per layout
+    and max(contiguous)/max(zigzag) measure what the layout is worth."""
+    import torch
+    from masked_attention_bdlm_amd.csbp import (ShareBuffers, clean_share_backward, clean_share_forward,
+                                                rank_blocks, rank_cost, share_backward, share_forward)
+    from synth import make_share_inputs
+
+    R, B, nb = w.share_ranks, w.block, w.seqlen // w.block
+    x = make_share_inputs(w, device=dev, nlocal=nb // R)     # input values do not affect the timing
+    bufs = ShareBuffers(x["qx"], x["kc"], x["kx"])
+    cbufs = ShareBuffers(x["qs"], x["kc"])
+    res = {}
+    for layout in ("contiguous", "zigzag"):
+        per = []
+        for r in range(R):
+            ids = rank_blocks(nb, R, r, layout)
+
+            def step(ids=ids):
+                o, lse = share_forward(x["qx"], x["kx"], x["vx"], x["kc"], x["vc"], ids, B, w.share_chunk,
+                                       w.scale, bufs, stream)
+                share_backward(x["qx"], x["kx"], x["vx"], x["kc"], x["vc"], ids, B, w.share_chunk, o, lse,
+                               x["dox"], w.scale, bufs, stream)
+                oc, lc = clean_share_forward(x["qs"], x["kc"], x["vc"], ids, B, w.share_chunk, w.scale, cbufs,
+                                             stream)
+                clean_share_backward(x["qs"], x["kc"], x["vc"], ids, B, w.share_chunk, oc, lc, x["dos"], w.scale,
+                                     cbufs, stream)
+
+            ms, _, _ = time_steps(step, args.steps, args.warmup, launches_per_step=8 * 2 * (nb * B // w.share_chunk + 1) + 32)
+            per.append({"rank": r, "blocks": ids, "ms": round(ms, 3), "block_pairs": 2 * rank_cost(ids)})
+            log(f"{layout} rank {r}: {ms:.2f} ms")
+        t = [p["ms"] for p in per]
+        res[layout] = {"max_ms": max(t), "mean_ms": round(sum(t) / R, 3), "min_ms": min(t),
+                       "max_over_mean": round(max(t) / (sum(t) / R), 4),
+                       "cost_max_over_mean": round(max(p["block_pairs"] for p in per) /
+                                                   (sum(p["block_pairs"] for p in per) / R), 4),
+                       "ranks": per}
+    speed = res["contiguous"]["max_ms"] / res["zigzag"]["max_ms"]
+    out = {
+        "metric": f"CSBP layer attention step time over {R} simulated ranks at 256K: slowest rank, "
+                  "contiguous vs zigzag block layout (speedup)",
+        "value": round(speed, 4), "unit": "x", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "clean_len": w.seqlen, "block": B, "ranks": R,
+                   "blocks_per_rank": nb // R, "chunk": w.share_chunk, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": w.head_dim, "parallelism": "single GPU (ranks timed one after another)"},
+        "layouts": res,
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +301,8 @@ def main():
     ap.add_argument("--workload", default="gqa_64k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--balance", action="store_true",
+                    help="with a rank-share workload: time all ranks under the contiguous and zigzag layouts")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter calibration)")
     args = ap.parse_args()
@@ -276,6 +334,12 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if w.share_blocks and args.balance:
+        if not w.clean_share:
+            print("--balance needs a workload with the clean query shard (csbp_rank_256k)", file=sys.stderr)
+            sys.exit(2)
+        bench_balance(args, w, dev, stream)
+        return
     if w.share_blocks:
         bench_share(args, w, dev, stream)
         return

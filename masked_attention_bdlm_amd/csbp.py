@@ -155,3 +155,29 @@ def clean_share_backward(qs, kc, vc, ids: Sequence[int], B: int, chunk: int, o, 
         bdlm_attn_bwd(d, None, kc, vc, qs, None, None, None, o, None, lse, None, dos,
                       None, bufs.dkc, bufs.dvc, bufs.dqx, None, None, bufs.ws, stream)
     return bufs.dqx, bufs.dkc, bufs.dvc
+
+
+# ------------------------------------------------------------------ rank layout
+def rank_blocks(nblocks: int, nranks: int, rank: int, layout: str = "zigzag") -> List[int]:
+    """Blocks a rank owns (its corrupted target blocks and its shard of the
+    clean sequence).  Block b costs b + 1 block-pairs in either half (a
+    corrupted block sees b clean blocks plus itself; a clean block sees the
+    clean blocks up to itself), so a contiguous cut loads the last rank about
+    twice the mean.  "zigzag" cuts the blocks into 2R equal runs and gives
+    rank r runs r and 2R-1-r, which equalises the cost exactly; "contiguous"
+    gives rank r the r-th of R equal runs."""
+    if nblocks % (2 * nranks) or not 0 <= rank < nranks:
+        raise ValueError("need nblocks % (2*nranks) == 0 and 0 <= rank < nranks")
+    if layout == "contiguous":
+        run = nblocks // nranks
+        return list(range(rank * run, (rank + 1) * run))
+    if layout != "zigzag":
+        raise ValueError(f"unknown layout {layout!r}")
+    run = nblocks // (2 * nranks)
+    return list(range(rank * run, (rank + 1) * run)) + \
+        list(range((2 * nranks - 1 - rank) * run, (2 * nranks - rank) * run))
+
+
+def rank_cost(ids: Sequence[int]) -> int:
+    """Visible block-pairs of a rank's blocks in one half of its share."""
+    return sum(int(b) + 1 for b in ids)

@@ -133,6 +133,52 @@ def test_clean_query_share_chunked_merge_and_backward(dtype, L, B, n, chunk, sha
     check_outputs(got, ref, dtype, where="clean-query share")
 
 
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+def test_csbp_ranks_assemble_to_full_attention(layout):
+    """CSBP over R simulated ranks on one GPU: each rank runs its corrupted
+    blocks and its clean query shard against the streamed clean K/V; the
+    assembled outputs, the per-block gradients and the clean dK/dV summed over
+    ranks (the reduce-scatter) equal full BDLM attention over [x0 ; xt]."""
+    from masked_attention_bdlm_amd import csbp
+    require_gpu()
+    L, B, R, chunk = 1024, 64, 4, 256
+    w = Workload(name="csbp_ranks", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=128, dtype="bf16",
+                 seed=17, q_std=128 ** -0.5)
+    announce(f"csbp ranks {layout} L={L} B={B} R={R} chunk={chunk}")
+    x = make_full_inputs(w, device="cuda")
+    got = {k: torch.zeros_like(x[s]) for k, s in (("oc", "qc"), ("ox", "qx"))}
+    got.update({k: torch.zeros((1, w.hq, L), dtype=torch.float32, device="cuda") for k in ("lse_c", "lse_x")})
+    got.update({k: torch.zeros(x["qc"].shape, dtype=torch.float32, device="cuda") for k in ("dqc", "dqx")})
+    got.update({k: torch.zeros(x["kc"].shape, dtype=torch.float32, device="cuda") for k in ("dkc", "dvc", "dkx", "dvx")})
+    for r in range(R):
+        ids = csbp.rank_blocks(L // B, R, r, layout)
+        rows = torch.cat([torch.arange(b * B, (b + 1) * B) for b in ids]).cuda()
+        sub = {k: x[k][:, rows].contiguous() for k in ("qc", "qx", "kx", "vx", "doc", "dox")}
+        cb = csbp.ShareBuffers(sub["qx"], x["kc"], sub["kx"])
+        o, lse = csbp.share_forward(sub["qx"], sub["kx"], sub["vx"], x["kc"], x["vc"], ids, B, chunk, w.scale, cb)
+        dq, dkc, dvc, dkx, dvx = csbp.share_backward(sub["qx"], sub["kx"], sub["vx"], x["kc"], x["vc"], ids, B,
+                                                     chunk, o, lse, sub["dox"], w.scale, cb)
+        got["ox"][:, rows] = o
+        got["lse_x"][:, :, rows] = lse
+        got["dqx"][:, rows] = dq
+        got["dkx"][:, rows] = dkx.float()
+        got["dvx"][:, rows] = dvx.float()
+        got["dkc"] += dkc.float()
+        got["dvc"] += dvc.float()
+        qb = csbp.ShareBuffers(sub["qc"], x["kc"])
+        o, lse = csbp.clean_share_forward(sub["qc"], x["kc"], x["vc"], ids, B, chunk, w.scale, qb)
+        dq, dkc, dvc = csbp.clean_share_backward(sub["qc"], x["kc"], x["vc"], ids, B, chunk, o, lse, sub["doc"],
+                                                 w.scale, qb)
+        got["oc"][:, rows] = o
+        got["lse_c"][:, :, rows] = lse
+        got["dqc"][:, rows] = dq
+        got["dkc"] += dkc.float()
+        got["dvc"] += dvc.float()
+    torch.cuda.synchronize()
+    ref = _oracle_full(host(x), B, w.scale)
+    check_outputs(host(got), ref, "bf16", where=f"csbp ranks {layout}")
+
+
 def test_share_partial_of_empty_window_is_minus_inf():
     require_gpu()
     w = Workload(name="share_empty", batch=1, seqlen=1024, block=64, hq=2, hkv=1, head_dim=64,

@@ -195,3 +195,19 @@ def test_masked_tiles_are_few_when_tiles_divide_blocks():
     assert st["masked_visits"] == 0
     _, stb = M.schedule_walk(desc, 1, want_cover=False)
     assert stb["masked_visits"] == 0
+
+
+def test_rank_layouts_partition_and_balance():
+    from masked_attention_bdlm_amd import csbp
+    from synth import clean_shard_ids
+    nb, R = 256, 16
+    for layout in ("zigzag", "contiguous"):
+        shards = [csbp.rank_blocks(nb, R, r, layout) for r in range(R)]
+        assert sorted(b for s in shards for b in s) == list(range(nb))
+    z = [csbp.rank_cost(csbp.rank_blocks(nb, R, r)) for r in range(R)]
+    c = [csbp.rank_cost(csbp.rank_blocks(nb, R, r, "contiguous")) for r in range(R)]
+    assert max(z) == min(z) == sum(z) // R
+    assert sum(c) == sum(z) == 256 * 257 // 2                  # every block once: 1 + 2 + ... + 256
+    assert max(c) == sum(range(241, 257)) == 3976              # the last rank: 1.934 x the mean 2056
+    # the workload generator draws the same zigzag shard
+    assert list(clean_shard_ids(nb, R, 3)) == csbp.rank_blocks(nb, R, 3)
