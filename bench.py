@@ -147,7 +147,8 @@ def step_stats(per_step):
 
 def bench_share(args, w, dev, stream):
     """One rank's CSBP share at its real shape: own-block partial, clean chunks
-    streamed with an in-place running merge, then the chunked backward.  Also
+    streamed with the running merge fused into the forward's epilogue, then the
+    chunked backward.  Also
     times one all-at-once merge of every partial a step produces (the merge
     kernel alone, HBM-bound)."""
     import torch

@@ -92,6 +92,12 @@ typedef struct {
      to the window; own_block must be 0.  0 = corrupted blocks (strict clean
      prefix).  Must be 0 in full mode.                                           */
   int32_t clean_queries;
+  /* Share mode, forward only (the backward ignores it): 1 = merge this call's
+     partial into the (O, LSE) that ox / lse_x already hold from earlier calls
+     of the same stream of chunks, in place (the running merge fused into the
+     kernel's epilogue); 0 = overwrite them with this call's partial.  Must be 0
+     in full mode. */
+  int32_t accumulate;
 } bdlm_attn_desc;
 
 /* Bytes of scratch memory a call needs (0 is possible).  for_bwd selects
@@ -120,7 +126,14 @@ int bdlm_attn_check_desc(const bdlm_attn_desc* desc);
  *   Parallelism ..., Sec. 4 and Fig. 3, the clean sequence sharded across the
  *   ranks in context-parallel form).  Writes the PARTIAL result over exactly those keys
  *   to ox (fp32, [batch, n*B, Hq, d]) and lse_x (fp32, [batch, Hq, n*B]); rows
- *   that see no key get O = 0 and LSE = -inf.
+ *   that see no key get O = 0 and LSE = -inf.  With accumulate = 1 the partial
+ *   is instead merged into the (O, LSE) that ox / lse_x hold: LSE becomes
+ *   logsumexp(LSE_held, LSE_part) and O the exp(LSE_j - LSE)-weighted sum of the
+ *   two (pages: the clean prefix streamed in chunks and the per-block results
+ *   combined, Sec. 4 / Fig. 3 as the review describes CSBP); rows that see no
+ *   key in this call are left as they are.  The caller starts a stream of
+ *   chunks with accumulate = 0 and must not run two accumulating calls on the
+ *   same ox / lse_x at once.
  */
 int bdlm_attn_fwd(const bdlm_attn_desc* desc,
                   const void* qc, const void* kc, const void* vc,

@@ -33,7 +33,7 @@ class BdlmDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("num_local_blocks", ctypes.c_int32), ("block_ids", ctypes.POINTER(ctypes.c_int32)),
         ("kv_begin", ctypes.c_int32), ("kv_end", ctypes.c_int32), ("own_block", ctypes.c_int32),
-        ("clean_queries", ctypes.c_int32),
+        ("clean_queries", ctypes.c_int32), ("accumulate", ctypes.c_int32),
     ]
 
 
@@ -96,7 +96,7 @@ def check(fn: str, status: int) -> None:
 
 
 def make_desc(batch, seqlen, block, hq, hkv, head_dim, dtype, scale, block_ids=None,
-              kv_begin=0, kv_end=0, own_block=0, clean_queries=0):
+              kv_begin=0, kv_end=0, own_block=0, clean_queries=0, accumulate=0):
     """Build a descriptor; keeps the host block-id array alive on the object."""
     d = BdlmDesc()
     d.batch, d.seqlen, d.block = int(batch), int(seqlen), int(block)
@@ -110,8 +110,10 @@ def make_desc(batch, seqlen, block, hq, hkv, head_dim, dtype, scale, block_ids=N
         d.block_ids = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
         d.kv_begin, d.kv_end, d.own_block = int(kv_begin), int(kv_end), int(own_block)
         d.clean_queries = int(clean_queries)
+        d.accumulate = int(accumulate)
     else:
         d.num_local_blocks = 0
         d.block_ids = None
         d.clean_queries = int(clean_queries)
+        d.accumulate = int(accumulate)
     return d

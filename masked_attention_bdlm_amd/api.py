@@ -42,7 +42,7 @@ def dtype_code(dt: torch.dtype) -> int:
 
 def desc_for(q: torch.Tensor, k: torch.Tensor, block: int, scale: Optional[float] = None,
              seqlen: Optional[int] = None, block_ids=None, kv_begin=0, kv_end=0, own_block=0,
-             clean_queries=0):
+             clean_queries=0, accumulate=0):
     """Descriptor from Q [batch, tokens, Hq, d] and K [batch, L, Hkv, d]."""
     b, _, hq, d = q.shape
     hkv = k.shape[2]
@@ -50,7 +50,7 @@ def desc_for(q: torch.Tensor, k: torch.Tensor, block: int, scale: Optional[float
     if scale is None:
         scale = d ** -0.5
     return make_desc(b, L, block, hq, hkv, d, dtype_code(q.dtype), scale, block_ids,
-                     kv_begin, kv_end, own_block, clean_queries)
+                     kv_begin, kv_end, own_block, clean_queries, accumulate)
 
 
 # ---------------------------------------------------------------- C-ABI calls
@@ -122,13 +122,15 @@ def attention_bwd(qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox, block:
 
 
 def share_fwd(qx, kx, vx, kc, vc, block_ids, block: int, kv_begin: int, kv_end: int,
-              own_block: int, scale: Optional[float] = None, out=None, stream=None, clean_queries: int = 0):
+              own_block: int, scale: Optional[float] = None, out=None, stream=None, clean_queries: int = 0,
+              accumulate: int = 0):
     """Share-mode partial over one key window: returns (O_part fp32, LSE_part).
 
     clean_queries=1: qx holds clean query blocks (each sees the clean keys of its
-    own and every earlier block); kx, vx may then be None."""
+    own and every earlier block); kx, vx may then be None.  accumulate=1: merge
+    the partial into the (O, LSE) already held in `out` instead."""
     desc = desc_for(qx, kc, block, scale, block_ids=block_ids, kv_begin=kv_begin, kv_end=kv_end,
-                    own_block=own_block, clean_queries=clean_queries)
+                    own_block=own_block, clean_queries=clean_queries, accumulate=accumulate)
     b, T, hq, d = qx.shape
     if out is None:
         o = torch.empty((b, T, hq, d), dtype=torch.float32, device=qx.device)

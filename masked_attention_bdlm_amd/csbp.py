@@ -6,9 +6,10 @@ chunks ("Block Parallelism For Efficient Distributed Long-Context Diffusion
 Language Model Training": abstract; review FAQ "What is CSBP?").  This module
 drives that stream with the C-ABI calls:
 
-forward   own-block partial, then per clean chunk a share-mode partial merged
-          into the running (O, LSE) in place; the last merge writes O in the
-          input dtype.
+forward   own-block partial, then per clean chunk a share-mode forward that
+          merges its partial into the running (O, LSE) in place, inside the
+          kernel's epilogue (accumulate = 1); a final one-part merge writes O in
+          the input dtype.
 backward  per clean chunk a share-mode backward with the final O and LSE (dQ
           added into one fp32 buffer, the chunk's clean dK/dV written at its
           window), plus the own-block backward.
@@ -40,8 +41,6 @@ class ShareBuffers:
         dev = qx.device
         self.acc_o = torch.empty((b, T, hq, d), dtype=torch.float32, device=dev)
         self.acc_lse = torch.empty((b, hq, T), dtype=torch.float32, device=dev)
-        self.part_o = torch.empty_like(self.acc_o)
-        self.part_lse = torch.empty_like(self.acc_lse)
         self.o = torch.empty_like(qx)
         self.lse = torch.empty_like(self.acc_lse)
         self.dqx = torch.empty((b, T, hq, d), dtype=torch.float32, device=dev)
@@ -70,10 +69,9 @@ def share_forward(qx, kx, vx, kc, vc, ids: Sequence[int], B: int, chunk: int,
     d_own = desc_for(qx, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=0, kv_end=0, own_block=1)
     bdlm_attn_fwd(d_own, None, kc, vc, qx, kx, vx, None, bufs.acc_o, None, bufs.acc_lse, None, stream)
     for (j0, j1) in _chunks(L, chunk, ids, B):
-        d = desc_for(qx, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=j0, kv_end=j1, own_block=0)
-        bdlm_attn_fwd(d, None, kc, vc, qx, kx, vx, None, bufs.part_o, None, bufs.part_lse, None, stream)
-        bdlm_attn_merge_partials([bufs.acc_o, bufs.part_o], [bufs.acc_lse, bufs.part_lse],
-                                 bufs.acc_o, bufs.acc_lse, stream)
+        d = desc_for(qx, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=j0, kv_end=j1, own_block=0,
+                     accumulate=1)
+        bdlm_attn_fwd(d, None, kc, vc, qx, kx, vx, None, bufs.acc_o, None, bufs.acc_lse, None, stream)
     bdlm_attn_merge_partials([bufs.acc_o], [bufs.acc_lse], bufs.o, bufs.lse, stream)
     return bufs.o, bufs.lse
 
@@ -119,16 +117,10 @@ def clean_share_forward(qs, kc, vc, ids: Sequence[int], B: int, chunk: int,
     ids = [int(i) for i in ids]
     L = kc.shape[1]
     bufs = bufs or ShareBuffers(qs, kc)
-    chunks = _clean_chunks(L, chunk, ids, B)
-    for n, (j0, j1) in enumerate(chunks):
+    for n, (j0, j1) in enumerate(_clean_chunks(L, chunk, ids, B)):
         d = desc_for(qs, kc, B, scale, seqlen=L, block_ids=ids, kv_begin=j0, kv_end=j1, own_block=0,
-                     clean_queries=1)
-        if n == 0:
-            bdlm_attn_fwd(d, None, kc, vc, qs, None, None, None, bufs.acc_o, None, bufs.acc_lse, None, stream)
-            continue
-        bdlm_attn_fwd(d, None, kc, vc, qs, None, None, None, bufs.part_o, None, bufs.part_lse, None, stream)
-        bdlm_attn_merge_partials([bufs.acc_o, bufs.part_o], [bufs.acc_lse, bufs.part_lse],
-                                 bufs.acc_o, bufs.acc_lse, stream)
+                     clean_queries=1, accumulate=int(n > 0))
+        bdlm_attn_fwd(d, None, kc, vc, qs, None, None, None, bufs.acc_o, None, bufs.acc_lse, None, stream)
     bdlm_attn_merge_partials([bufs.acc_o], [bufs.acc_lse], bufs.o, bufs.lse, stream)
     return bufs.o, bufs.lse
 

@@ -74,7 +74,8 @@ int check_desc(const bdlm_attn_desc* d) {
     if (d->own_block != 0 && d->own_block != 1) return BDLM_ERR_INVALID_ARG;
     if (d->clean_queries != 0 && d->clean_queries != 1) return BDLM_ERR_INVALID_ARG;
     if (d->clean_queries && d->own_block) return BDLM_ERR_INVALID_ARG;
-  } else if (d->clean_queries != 0) {
+    if (d->accumulate != 0 && d->accumulate != 1) return BDLM_ERR_INVALID_ARG;
+  } else if (d->clean_queries != 0 || d->accumulate != 0) {
     return BDLM_ERR_INVALID_ARG;
   }
   return BDLM_OK;
@@ -193,6 +194,7 @@ int bdlm_attn_fwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   a.lse[0] = lse_c; a.lse[1] = lse_x;
   a.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
   a.ns0 = share ? 1 : 0;
+  a.accum = share ? desc->accumulate : 0;
   for (int s = 0; s < 2; ++s) a.nqt[s] = (a.p.rows[s] + kFwdTileM - 1) / kFwdTileM;
   const int nstr = 2 - a.ns0;
   const int per_bg = a.nqt[1] * nstr * a.p.group;

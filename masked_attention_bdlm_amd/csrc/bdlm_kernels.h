@@ -18,6 +18,7 @@ struct FwdArgs {
   float scale_log2;     // softmax_scale * log2(e)
   int nqt[2];           // 128-row query tiles per stream
   int ns0;              // first stream with queries (0 full, 1 share)
+  int accum;            // share mode: merge into the (O, LSE) already in o/lse (fp32 O)
   XcdMap map;
 };
 

@@ -312,21 +312,52 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
 
   const float l_tot = l_run + wave_swap32(l_run);
   if (valid) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float lse_out = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     using OT = typename std::conditional<OUT_F32, float, T>::type;
     OT* orow = reinterpret_cast<OT*>(args.o[s]) + ((int64_t)b * R + r) * p.hq * D + (int64_t)h * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        OT* dst = orow + dt * 32 + g4 * 8 + hh * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = static_cast<OT>(oacc[dt][g4 * 4 + j] * inv);
+    float* lrow = &args.lse[s][((int64_t)b * p.hq + h) * R + r];
+    bool write = true;
+    float w_old = 0.f;
+    if constexpr (OUT_F32) {
+      // Running merge of this call's partial into the held one (fp32 O): both
+      // are normalised attention outputs over disjoint key sets, so
+      // LSE = logsumexp(LSE_old, LSE_new) and O = sum_j exp(LSE_j - LSE) O_j.
+      // A row that sees no key here keeps the held result unchanged.
+      if (args.accum) {
+        if (l_tot > 0.f) {
+          const float lse_old = *lrow;
+          const float m = fmaxf(lse_old, lse_out);
+          const float a_old = __expf(lse_old - m);   // 0 when nothing is held yet
+          const float a_new = __expf(lse_out - m);
+          const float sum = a_old + a_new;
+          w_old = a_old / sum;
+          inv *= a_new / sum;
+          lse_out = m + __logf(sum);
+        } else {
+          write = false;
+        }
       }
     }
-    if (hh == 0) {
-      args.lse[s][((int64_t)b * p.hq + h) * R + r] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (write) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          OT* dst = orow + dt * 32 + g4 * 8 + hh * 4;
+          if constexpr (OUT_F32) {
+            if (w_old != 0.f) {   // only while merging into a held result
+              const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) dst[j] = w_old * old[j] + oacc[dt][g4 * 4 + j] * inv;
+              continue;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dst[j] = static_cast<OT>(oacc[dt][g4 * 4 + j] * inv);
+        }
+      }
+      if (hh == 0) *lrow = lse_out;
     }
   }
 }

@@ -179,6 +179,54 @@ def test_csbp_ranks_assemble_to_full_attention(layout):
     check_outputs(host(got), ref, "bf16", where=f"csbp ranks {layout}")
 
 
+@pytest.mark.parametrize("clean", [False, True])
+def test_fused_running_merge_matches_merge_kernel(clean):
+    """accumulate = 1 (the running merge inside the forward's epilogue) gives
+    the same (O, LSE) as separate partials merged by the merge kernel, and
+    equals the oracle's one pass; a window no block sees leaves the held result
+    bit-identical."""
+    from masked_attention_bdlm_amd import csbp
+    require_gpu()
+    L, B, n, chunk = 2048, 128, 4, 384
+    w = Workload(name="fused_merge", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=128, dtype="bf16",
+                 seed=19, q_std=128 ** -0.5, share_blocks=n, share_chunk=chunk)
+    announce(f"fused running merge clean={clean}")
+    x = make_share_inputs(w, device="cuda", sharp=True)
+    ids = [int(i) for i in x["block_ids"]]
+    q, kx, vx = x["qx"], (None if clean else x["kx"]), (None if clean else x["vx"])
+    own = 0 if clean else 1
+    wins = [(j, min(j + chunk, L)) for j in range(0, L, chunk)]
+    # fused: first call overwrites (the own block, or the first chunk), the rest accumulate
+    acc = M.share_fwd(q, kx, vx, x["kc"], x["vc"], ids, B, 0, 0 if own else wins[0][1], own, w.scale,
+                      clean_queries=int(clean))
+    rest = wins if own else wins[1:]
+    for j0, j1 in rest:
+        M.share_fwd(q, kx, vx, x["kc"], x["vc"], ids, B, j0, j1, 0, w.scale, out=acc, clean_queries=int(clean),
+                    accumulate=1)
+    # separate partials merged by the merge kernel
+    parts = [M.share_fwd(q, kx, vx, x["kc"], x["vc"], ids, B, 0, 0 if own else wins[0][1], own, w.scale,
+                         clean_queries=int(clean))]
+    parts += [M.share_fwd(q, kx, vx, x["kc"], x["vc"], ids, B, j0, j1, 0, w.scale, clean_queries=int(clean))
+              for j0, j1 in rest]
+    o_m, lse_m = M.merge_partials([p[0] for p in parts], [p[1] for p in parts], torch.float32)
+    torch.cuda.synchronize()
+    assert torch.allclose(acc[0], o_m, atol=2e-6, rtol=0), float((acc[0] - o_m).abs().max())
+    assert torch.allclose(acc[1], lse_m, atol=2e-6, rtol=0), float((acc[1] - lse_m).abs().max())
+    # a window above every prefix: nothing visible, the held result stays as it is
+    held_o, held_l = acc[0].clone(), acc[1].clone()
+    top = (max(ids) + (1 if clean else 0)) * B
+    if top < L:
+        M.share_fwd(q, kx, vx, x["kc"], x["vc"], ids, B, top, L, 0, w.scale, out=acc, clean_queries=int(clean),
+                    accumulate=1)
+        torch.cuda.synchronize()
+        assert torch.equal(acc[0], held_o) and torch.equal(acc[1], held_l)
+    xh = host(x)
+    o_ref, lse_ref = O.share_fwd(xh["qx"], xh["kx"], xh["vx"], xh["kc"], xh["vc"], ids, B, 0, L, own, w.scale,
+                                 clean_queries=clean)
+    check_outputs(host(dict(ox=acc[0], lse_x=acc[1])), dict(ox=o_ref, lse_x=lse_ref), "bf16",
+                  where="fused running merge")
+
+
 def test_share_partial_of_empty_window_is_minus_inf():
     require_gpu()
     w = Workload(name="share_empty", batch=1, seqlen=1024, block=64, hq=2, hkv=1, head_dim=64,

@@ -43,7 +43,7 @@ def _ok_desc(**kw):
     return make_desc(base["batch"], base["seqlen"], base["block"], base["hq"], base["hkv"],
                      base["head_dim"], base["dtype"], base["scale"], base.get("block_ids"),
                      base.get("kv_begin", 0), base.get("kv_end", 0), base.get("own_block", 0),
-                     base.get("clean_queries", 0))
+                     base.get("clean_queries", 0), base.get("accumulate", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -68,6 +68,9 @@ def _ok_desc(**kw):
     ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "clean_queries": 1, "own_block": 1}, 1),
     ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "clean_queries": 2}, 1),
     ({"clean_queries": 1}, 1),       # clean-query rule needs share mode
+    ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "accumulate": 1}, 0),
+    ({"block_ids": [1, 5], "kv_begin": 0, "kv_end": 64, "accumulate": 3}, 1),
+    ({"accumulate": 1}, 1),          # running merge needs share mode
     ({"seqlen": 8192, "block": 16, "block_ids": list(range(300)), "kv_begin": 0, "kv_end": 16}, 2),
 ])
 def test_descriptor_validation(kw, code):
