@@ -79,16 +79,18 @@ def _share_flow(x, ids, L, B, chunk, scale, out_dtype):
     return dict(ox=o_fin, lse_x=lse_fin, dqx=dqx, dkc=dkc, dvc=dvc, dkx=dkx, dvx=dvx)
 
 
-@pytest.mark.parametrize("dtype,L,B,n,chunk,sharp", [
-    ("bf16", 2048, 128, 4, 512, False),
-    ("bf16", 2048, 128, 4, 384, True),      # chunks not aligned to blocks
-    ("bf16", 1024, 64, 5, 256, True),
-    ("f32", 1024, 64, 3, 320, False),
+@pytest.mark.parametrize("dtype,L,B,n,chunk,sharp,d", [
+    ("bf16", 2048, 128, 4, 512, False, 128),
+    ("bf16", 2048, 128, 4, 384, True, 128),      # chunks not aligned to blocks
+    ("bf16", 1024, 64, 5, 256, True, 128),
+    ("f32", 1024, 64, 3, 320, False, 128),
+    ("bf16", 1024, 64, 4, 320, True, 64),        # head_dim 64
+    ("f32", 512, 32, 3, 96, False, 64),
 ])
-def test_share_mode_chunked_merge_and_backward(dtype, L, B, n, chunk, sharp):
+def test_share_mode_chunked_merge_and_backward(dtype, L, B, n, chunk, sharp, d):
     require_gpu()
-    w = Workload(name="share_small", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=128,
-                 dtype=dtype, seed=11, q_std=128 ** -0.5, share_blocks=n, share_chunk=chunk)
+    w = Workload(name="share_small", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=d,
+                 dtype=dtype, seed=11, q_std=d ** -0.5, share_blocks=n, share_chunk=chunk)
     announce(f"share {dtype} L={L} B={B} n={n} chunk={chunk} sharp={sharp}")
     x = make_share_inputs(w, device="cuda", sharp=sharp)
     ids = [int(i) for i in x["block_ids"]]
@@ -102,19 +104,21 @@ def test_share_mode_chunked_merge_and_backward(dtype, L, B, n, chunk, sharp):
     check_outputs(got, ref, dtype, where="share")
 
 
-@pytest.mark.parametrize("dtype,L,B,n,chunk,sharp", [
-    ("bf16", 2048, 128, 4, 512, False),
-    ("bf16", 1024, 64, 5, 384, True),       # chunks not aligned to blocks
-    ("f32", 1024, 64, 3, 320, False),
+@pytest.mark.parametrize("dtype,L,B,n,chunk,sharp,d", [
+    ("bf16", 2048, 128, 4, 512, False, 128),
+    ("bf16", 1024, 64, 5, 384, True, 128),       # chunks not aligned to blocks
+    ("f32", 1024, 64, 3, 320, False, 128),
+    ("bf16", 1024, 64, 4, 256, True, 64),        # head_dim 64
+    ("f32", 512, 32, 3, 96, False, 64),
 ])
-def test_clean_query_share_chunked_merge_and_backward(dtype, L, B, n, chunk, sharp):
+def test_clean_query_share_chunked_merge_and_backward(dtype, L, B, n, chunk, sharp, d):
     """The rank's clean query blocks (clean_queries = 1: own and earlier clean
     blocks visible, no corrupted keys) streamed over clean chunks with the
     running merge, then the chunked backward, against the oracle's one pass."""
     from masked_attention_bdlm_amd import csbp
     require_gpu()
-    w = Workload(name="clean_share_small", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=128,
-                 dtype=dtype, seed=13, q_std=128 ** -0.5, share_blocks=n, share_chunk=chunk)
+    w = Workload(name="clean_share_small", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=d,
+                 dtype=dtype, seed=13, q_std=d ** -0.5, share_blocks=n, share_chunk=chunk)
     announce(f"clean-query share {dtype} L={L} B={B} n={n} chunk={chunk} sharp={sharp}")
     x = make_share_inputs(w, device="cuda", sharp=sharp)
     ids = [int(i) for i in x["block_ids"]]
@@ -179,8 +183,9 @@ def test_csbp_ranks_assemble_to_full_attention(layout):
     check_outputs(host(got), ref, "bf16", where=f"csbp ranks {layout}")
 
 
-@pytest.mark.parametrize("clean", [False, True])
-def test_fused_running_merge_matches_merge_kernel(clean):
+@pytest.mark.parametrize("clean,d,dtype", [(False, 128, "bf16"), (True, 128, "bf16"), (False, 64, "bf16"),
+                                           (True, 64, "f32")])
+def test_fused_running_merge_matches_merge_kernel(clean, d, dtype):
     """accumulate = 1 (the running merge inside the forward's epilogue) gives
     the same (O, LSE) as separate partials merged by the merge kernel, and
     equals the oracle's one pass; a window no block sees leaves the held result
@@ -188,9 +193,9 @@ def test_fused_running_merge_matches_merge_kernel(clean):
     from masked_attention_bdlm_amd import csbp
     require_gpu()
     L, B, n, chunk = 2048, 128, 4, 384
-    w = Workload(name="fused_merge", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=128, dtype="bf16",
-                 seed=19, q_std=128 ** -0.5, share_blocks=n, share_chunk=chunk)
-    announce(f"fused running merge clean={clean}")
+    w = Workload(name="fused_merge", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=d, dtype=dtype,
+                 seed=19, q_std=d ** -0.5, share_blocks=n, share_chunk=chunk)
+    announce(f"fused running merge clean={clean} d={d} {dtype}")
     x = make_share_inputs(w, device="cuda", sharp=True)
     ids = [int(i) for i in x["block_ids"]]
     q, kx, vx = x["qx"], (None if clean else x["kx"]), (None if clean else x["vx"])
@@ -223,7 +228,7 @@ def test_fused_running_merge_matches_merge_kernel(clean):
     xh = host(x)
     o_ref, lse_ref = O.share_fwd(xh["qx"], xh["kx"], xh["vx"], xh["kc"], xh["vc"], ids, B, 0, L, own, w.scale,
                                  clean_queries=clean)
-    check_outputs(host(dict(ox=acc[0], lse_x=acc[1])), dict(ox=o_ref, lse_x=lse_ref), "bf16",
+    check_outputs(host(dict(ox=acc[0], lse_x=acc[1])), dict(ox=o_ref, lse_x=lse_ref), dtype,
                   where="fused running merge")
 
 
