@@ -247,6 +247,22 @@ __device__ inline void dma_rows(T* tile, const T* base, int64_t rs, int k0, int 
   static_assert(NR % S::RPB == 0, "tile rows must fill whole DMA blocks");
   static_assert(NBLK % NW == 0, "every wave issues the same number of blocks");
   const int lr = lane / S::CH, pc = lane % S::CH;
+  if (k0 + NR <= kmax) {
+    // Whole tile inside the array: one uniform base (scalar registers) plus a
+    // 32-bit per-lane byte offset that does not depend on k0, so the address
+    // costs no per-lane 64-bit arithmetic.
+    const char* tb = reinterpret_cast<const char*>(base + (int64_t)k0 * rs);
+#pragma unroll
+    for (int j = 0; j < NBLK / NW; ++j) {
+      const int bb = wave + j * NW;
+      const int r = bb * S::RPB + lr;
+      const int c = pc ^ S::f(r);
+      const uint32_t off = ((uint32_t)r * (uint32_t)rs + (uint32_t)(c * S::EPC)) * (uint32_t)sizeof(T);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tb + off),
+                                       (__attribute__((address_space(3))) void*)(tile + bb * S::RPB * D), 16, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NBLK / NW; ++j) {
     const int bb = wave + j * NW;

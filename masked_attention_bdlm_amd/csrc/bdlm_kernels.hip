@@ -234,19 +234,22 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    // Edge tiles only (one uniform branch): keys outside the row's range.
+    if (need_mask) {
+#pragma unroll
+      for (int sub = 0; sub < N / 32; ++sub) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = k0 + sub * 32 + c_row(i, hh);
+          if (kk < mylo || kk >= myhi) sacc[sub][i] = -INFINITY;
+        }
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < N / 32; ++sub) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = sacc[sub][i];
-        if (need_mask) {
-          const int kk = k0 + sub * 32 + c_row(i, hh);
-          if (kk < mylo || kk >= myhi) v = -INFINITY;
-        }
-        sacc[sub][i] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[sub][i]);
     }
     mx = fmaxf(mx, wave_swap32(mx));
     // Lazy rescaling: O and l stay relative to the reference m_run until some
@@ -1153,20 +1156,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
         dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, lane);
       }
       __builtin_amdgcn_sched_barrier(0);
+      float pe[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pe[i] = fast_exp2(sacc[i] * args.scale_log2 - lse2);
+      // Edge tiles only (one uniform branch): keys outside the row's range.
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = k0 + sub * 32 + c_row(i, hh);
+          if (kk < mylo || kk >= myhi) pe[i] = 0.f;
+        }
+      }
       Frag dsf[CPS];
 #pragma unroll
       for (int ci = 0; ci < CPS; ++ci) {
         float de[KPL];
 #pragma unroll
-        for (int jj = 0; jj < KPL; ++jj) {
-          const int i = ci * KPL + jj;
-          float e = fast_exp2(sacc[i] * args.scale_log2 - lse2);
-          if (need_mask) {
-            const int kk = k0 + sub * 32 + c_row(i, hh);
-            if (kk < mylo || kk >= myhi) e = 0.f;
-          }
-          de[jj] = e * (pacc[i] - dd);
-        }
+        for (int jj = 0; jj < KPL; ++jj) de[jj] = pe[ci * KPL + jj] * (pacc[ci * KPL + jj] - dd);
         dsf[ci] = pack_frag<T>(de);
       }
       // dQ^T[d][query] += K^T[d][key] dS^T[key][query]
