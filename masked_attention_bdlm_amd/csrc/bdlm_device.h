@@ -331,7 +331,20 @@ template <> __device__ inline void store_crow_run<float>(float* row, int ci, int
 
 template <typename T> __device__ inline T to_elt(float x) { return static_cast<T>(x); }
 
-__device__ inline float wave_swap32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine the two 32-lane halves of a wave64 lane by lane: lane l gets
+// op(x[l mod 32], x[l mod 32 + 32]).  v_permlane32_swap exchanges 32 lanes
+// between its two register operands; with x in both, one result holds the
+// lower half twice and the other the upper half twice, so a symmetric op of
+// the two results needs no lane select (and no LDS round trip, unlike a
+// ds_bpermute shuffle).
+__device__ inline float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[sub][i]);
     }
-    mx = fmaxf(mx, wave_swap32(mx));
+    mx = halves_max(mx);
     // Lazy rescaling: O and l stay relative to the reference m_run until some
     // row's max exceeds it by more than 8 (log2 units); the exponentials are
     // then at most 2^8, harmless for fp32 sums and bf16 operands, and the
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
     }
   }
 
-  const float l_tot = l_run + wave_swap32(l_run);
+  const float l_tot = halves_sum(l_run);
   if (valid) {
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float lse_out = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
@@ -847,13 +847,22 @@ __global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
         WS_GET(it, e);
         // S and dP for rows qs*32 .. +31 (rows = queries, column = this lane's key)
         f32x16 sacc = f32x16{}, pacc = f32x16{};
+        // Q / dO fragments read two k-chunks ahead of their MFMAs (3-slot ring)
+        bf16x8 qa[3], da[3];
+        auto rd = [&](int c) {
+          const char* ap = tb + offA[c] + qs * 32 * D * 2;
+          qa[c % 3] = *reinterpret_cast<const bf16x8*>(ap);
+          da[c % 3] = *reinterpret_cast<const bf16x8*>(ap + L::TILE);
+        };
+        rd(0);
+        if (L::DCH > 1) rd(1);
 #pragma unroll
         for (int c = 0; c < L::DCH; ++c) {
-          const char* ap = tb + offA[c] + qs * 32 * D * 2;
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(ap);
-          const bf16x8 da = *reinterpret_cast<const bf16x8*>(ap + L::TILE);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[c], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[c], pacc, 0, 0, 0);
+          if (c + 2 < L::DCH) rd(c + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c % 3], kf[c], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[c % 3], vf[c], pacc, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         // P and dS in the C layout (k of the consumer's MFMAs = queries)
         const char* rb = tb + 2 * L::TILE;
@@ -960,22 +969,37 @@ __global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
           pfr[ci] = *reinterpret_cast<const bf16x8*>(pd + ci * 1024);
           sfr[ci] = *reinterpret_cast<const bf16x8*>(pd + 2048 + ci * 1024);
         }
-        // dV_w += P^T dO ; dK_w += dS^T Q
-#pragma unroll
-        for (int dt = 0; dt < L::DT; ++dt) {
+        // dV_w += P^T dO ; dK_w += dS^T Q.  The transposed dO / Q fragments of
+        // column block dt + 1 are read while the MFMAs of block dt run.
+        bf16x8 ob[2][2], qb[2][2];
+        auto read_t = [&](int dt, bf16x8 (&o)[2], bf16x8 (&q)[2]) {
 #pragma unroll
           for (int ci = 0; ci < 2; ++ci) {
             const int imm = (qs * 32 + 16 * ci) * D * 2;
             const char* b0 = tb + offT[2 * dt] + imm;
             const char* b1 = tb + offT[2 * dt + 1] + imm;
-            const bf16x8 ob = cat44(__builtin_bit_cast(bf16x4, ds_read_tr16(b0 + L::TILE)),
-                                    __builtin_bit_cast(bf16x4, ds_read_tr16(b1 + L::TILE)));
-            const bf16x8 qb = cat44(__builtin_bit_cast(bf16x4, ds_read_tr16(b0)),
-                                    __builtin_bit_cast(bf16x4, ds_read_tr16(b1)));
-            dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfr[ci], ob, dvacc[dt], 0, 0, 0);
-            dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sfr[ci], qb, dkacc[dt], 0, 0, 0);
+            o[ci] = cat44(__builtin_bit_cast(bf16x4, ds_read_tr16(b0 + L::TILE)),
+                          __builtin_bit_cast(bf16x4, ds_read_tr16(b1 + L::TILE)));
+            q[ci] = cat44(__builtin_bit_cast(bf16x4, ds_read_tr16(b0)),
+                          __builtin_bit_cast(bf16x4, ds_read_tr16(b1)));
           }
+        };
+        // (for block 0 after its first MFMA pair, behind the P/dS reads, so
+        // that at most 12 LDS reads are outstanding: the wait counter holds 15)
+        read_t(0, ob[0], qb[0]);
+#pragma unroll
+        for (int dt = 0; dt < L::DT; ++dt) {
+          if (dt >= 1 && dt + 1 < L::DT) read_t(dt + 1, ob[(dt + 1) & 1], qb[(dt + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfr[0], ob[dt & 1][0], dvacc[dt], 0, 0, 0);
+          dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sfr[0], qb[dt & 1][0], dkacc[dt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (dt == 0 && L::DT > 1) read_t(1, ob[1], qb[1]);
+          __builtin_amdgcn_sched_barrier(0);
+          dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfr[1], ob[dt & 1][1], dvacc[dt], 0, 0, 0);
+          dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sfr[1], qb[dt & 1][1], dkacc[dt], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (j & 1) {                                    // tile (j+1)/2 is read from step j+1 on
         const int i = (j + 1) / 2;
@@ -1147,6 +1171,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // The first d-tile's K^T fragments do not depend on dS: read them now,
+      // so that their latency hides behind the DMA issue and the exponentials.
+      Frag kt[2][CPS];
+#pragma unroll
+      for (int ci = 0; ci < CPS; ++ci) {
+        if constexpr (OFFS) kt[0][ci] = ld_fragT(reinterpret_cast<const char*>(k_lds), offT, 0, (sub * 32 + 16 * ci) * D * 2);
+        else kt[0][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, 0);
+      }
       // Next tile's DMA, issued behind the first sub-tile's S^T / dP^T MFMAs
       // (a wave stalls while the memory pipeline accepts DMA instructions).
       if (sub == 0 && it + 1 < total) {
@@ -1177,12 +1209,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
       }
       // dQ^T[d][query] += K^T[d][key] dS^T[key][query]
       {
-        Frag kt[2][CPS];
-#pragma unroll
-        for (int ci = 0; ci < CPS; ++ci) {
-          if constexpr (OFFS) kt[0][ci] = ld_fragT(reinterpret_cast<const char*>(k_lds), offT, 0, (sub * 32 + 16 * ci) * D * 2);
-          else kt[0][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, 0);
-        }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           if (dt + 1 < D / 32) {
