@@ -854,30 +854,39 @@ __global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
           qa[c % 3] = *reinterpret_cast<const bf16x8*>(ap);
           da[c % 3] = *reinterpret_cast<const bf16x8*>(ap + L::TILE);
         };
+        // The rows' LSE and D values (C-layout rows of this lane) are read in
+        // the middle of the MFMA chain, so that they have landed at its end.
+        const char* rb = tb + 2 * L::TILE;
+        f32x4 lv[4], dv[4];
+        auto rd_rows = [&]() {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int rr = qs * 32 + 8 * i4 + 4 * hh;
+            lv[i4] = *reinterpret_cast<const f32x4*>(rb + rr * 4);
+            dv[i4] = *reinterpret_cast<const f32x4*>(rb + 256 + rr * 4);
+          }
+        };
         rd(0);
         if (L::DCH > 1) rd(1);
 #pragma unroll
         for (int c = 0; c < L::DCH; ++c) {
           if (c + 2 < L::DCH) rd(c + 2);
+          if (c == L::DCH / 2 - 1) rd_rows();
           __builtin_amdgcn_sched_barrier(0);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c % 3], kf[c], sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[c % 3], vf[c], pacc, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
         // P and dS in the C layout (k of the consumer's MFMAs = queries)
-        const char* rb = tb + 2 * L::TILE;
         float pe[16], de[16];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int rr = qs * 32 + 8 * i4 + 4 * hh;
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(rb + rr * 4);
-          const f32x4 dv = *reinterpret_cast<const f32x4*>(rb + 256 + rr * 4);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int i = 4 * i4 + jj;
-            const float ex = fast_exp2(__builtin_fmaf(sacc[i], sl2, -lv[jj]));
+            const float ex = fast_exp2(__builtin_fmaf(sacc[i], sl2, -lv[i4][jj]));
             pe[i] = ex;
-            de[i] = ex * (pacc[i] - dv[jj]);
+            de[i] = ex * (pacc[i] - dv[i4][jj]);
           }
         }
         if ((e >> 20) & 1u) {   // edge tile: each row's visible keys; rows past the stream end
