@@ -40,8 +40,8 @@ PEAK_HBM_GBS = 8000.0
 # the counters are taken again.
 MEASURED_TRAFFIC = {
     "kernel": "bdlm_dkdv",
-    "sources_sha256": "130d6f129b54cd252a3f2a875cfb49db9bee8ac314941471689f20cfca3205cb",
-    "fetch_kib": 9.54e6, "fetch_scale": 2.0,
+    "sources_sha256": "4af40bfe7203de2b85a860fe1c4ca0efdd7ea777754715c13cf983ab41fa6d13",
+    "fetch_kib": 9.297e6, "fetch_scale": 2.0,
     "write_kib": 2.621e5, "write_scale": 1.0,
 }
 KERNEL_SOURCES = ["bdlm_kernels.hip", "bdlm_kernels.h", "bdlm_device.h", "bdlm_common.h"]
