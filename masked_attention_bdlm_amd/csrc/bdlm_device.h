@@ -247,32 +247,35 @@ __device__ inline void dma_rows(T* tile, const T* base, int64_t rs, int k0, int 
   static_assert(NR % S::RPB == 0, "tile rows must fill whole DMA blocks");
   static_assert(NBLK % NW == 0, "every wave issues the same number of blocks");
   const int lr = lane / S::CH, pc = lane % S::CH;
-  if (k0 + NR <= kmax) {
-    // Whole tile inside the array: one uniform base (scalar registers) plus a
-    // 32-bit per-lane byte offset that does not depend on k0, so the address
-    // costs no per-lane 64-bit arithmetic.
-    const char* tb = reinterpret_cast<const char*>(base + (int64_t)k0 * rs);
+  // Every address is one wave-uniform base (row k0, scalar registers) plus a
+  // 32-bit per-lane byte offset: the instruction then takes the scalar-base
+  // form, whose per-lane address is 4 bytes instead of 8, which the memory
+  // pipeline accepts faster.  The empty asm keeps the compiler from widening
+  // the (loop-invariant) offset into a 64-bit per-lane address.
+  const char* tb = reinterpret_cast<const char*>(base + (int64_t)k0 * rs);
+  if (k0 + NR <= kmax) {   // whole tile inside the array: fixed per-lane offsets
 #pragma unroll
     for (int j = 0; j < NBLK / NW; ++j) {
       const int bb = wave + j * NW;
       const int r = bb * S::RPB + lr;
       const int c = pc ^ S::f(r);
-      const uint32_t off = ((uint32_t)r * (uint32_t)rs + (uint32_t)(c * S::EPC)) * (uint32_t)sizeof(T);
+      uint32_t off = ((uint32_t)r * (uint32_t)rs + (uint32_t)(c * S::EPC)) * (uint32_t)sizeof(T);
+      asm volatile("" : "+v"(off));
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tb + off),
                                        (__attribute__((address_space(3))) void*)(tile + bb * S::RPB * D), 16, 0, 0);
     }
-    return;
-  }
+  } else {                 // the tile crosses the array end: rows clamped to kmax - 1
 #pragma unroll
-  for (int j = 0; j < NBLK / NW; ++j) {
-    const int bb = wave + j * NW;
-    const int r = bb * S::RPB + lr;
-    const int c = pc ^ S::f(r);
-    int k = k0 + r;
-    if (k >= kmax) k = kmax - 1;
-    const T* src = base + (int64_t)k * rs + c * S::EPC;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(tile + bb * S::RPB * D), 16, 0, 0);
+    for (int j = 0; j < NBLK / NW; ++j) {
+      const int bb = wave + j * NW;
+      const int r = bb * S::RPB + lr;
+      const int c = pc ^ S::f(r);
+      const int rr = min(r, kmax - 1 - k0);
+      uint32_t off = ((uint32_t)rr * (uint32_t)rs + (uint32_t)(c * S::EPC)) * (uint32_t)sizeof(T);
+      asm volatile("" : "+v"(off));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tb + off),
+                                       (__attribute__((address_space(3))) void*)(tile + bb * S::RPB * D), 16, 0, 0);
+    }
   }
 }
 

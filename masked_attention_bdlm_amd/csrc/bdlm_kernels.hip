@@ -949,9 +949,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
     dma_rows<bf16, M, D>(tq_, (s_ ? q_1 : q_0) + hb_, qrs, q0_, q1_, wy, lane);                  \
     dma_rows<bf16, M, D>(tq_ + M * D, (s_ ? do_1 : do_0) + hb_, qrs, q0_, q1_, wy, lane);        \
     if (wy < 2) {                                                                                \
-      const int64_t ri_ = ((int64_t)b * p.hq + h_) * R_ + min(q0_ + lane, q1_ - 1);              \
-      const float* src_ = (wy == 0 ? (s_ ? l2_1 : l2_0) : (s_ ? dl_1 : dl_0)) + ri_;             \
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src_,      \
+      const float* rb_ = (wy == 0 ? (s_ ? l2_1 : l2_0) : (s_ ? dl_1 : dl_0)) +                   \
+                         (((int64_t)b * p.hq + h_) * R_ + q0_);                                  \
+      uint32_t ro_ = 4u * (uint32_t)min(lane, q1_ - 1 - q0_);                                    \
+      asm volatile("" : "+v"(ro_));                                                              \
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)           \
+                                       (reinterpret_cast<const char*>(rb_) + ro_),               \
                                        (__attribute__((address_space(3))) void*)(smem +          \
                                            ((i) % L::NBUF) * L::BUFB + 2 * L::TILE + wy * 256), 4, 0, 0); \
     }                                                                                            \
