@@ -1305,46 +1305,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs args) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float tot = 0.f;
   constexpr int PB = 8;
-  // The rows of a wave almost always share their live set (they belong to one
-  // block); then the part index is wave-uniform and the parts' pointers are
-  // scalar loads instead of per-lane pointer gathers ahead of every data load.
-  const uint64_t wlive = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)live)) |
-                         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(live >> 32)) << 32);
-  if (__all(live == wlive)) {
-    uint64_t lv = wlive;
-    while (lv) {
-      int idx[PB];
-#pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        idx[u] = lv ? __builtin_ctzll(lv) : -1;
-        lv &= lv ? lv - 1 : 0ull;
-      }
-      float l[PB];
-      float4 v[PB];
-#pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        if (idx[u] >= 0) {
-          l[u] = args.lse[idx[u]][li];
-          v[u] = *reinterpret_cast<const float4*>(args.o[idx[u]] + oi);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        if (idx[u] >= 0) {
-          const float wj = __expf(l[u] - m);
-          tot += wj;
-          acc.x += wj * v[u].x; acc.y += wj * v[u].y; acc.z += wj * v[u].z; acc.w += wj * v[u].w;
-        }
-      }
-    }
-    live = 0;
-  }
-  while (live) {
+  // Takes the next (up to) PB live parts out of `set` and adds them in.
+  auto merge_batch = [&](uint64_t& set) {
     int idx[PB];
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      idx[u] = live ? __builtin_ctzll(live) : -1;
-      live &= live ? live - 1 : 0ull;
+      idx[u] = set ? __builtin_ctzll(set) : -1;
+      set &= set ? set - 1 : 0ull;
     }
     float l[PB];
     float4 v[PB];
@@ -1363,6 +1330,17 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs args) {
         acc.x += wj * v[u].x; acc.y += wj * v[u].y; acc.z += wj * v[u].z; acc.w += wj * v[u].w;
       }
     }
+  };
+  // The rows of a wave almost always share their live set (they belong to one
+  // block); then the part index is wave-uniform and the parts' pointers are
+  // scalar loads instead of per-lane pointer gathers ahead of every data load.
+  const uint64_t wlive = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)live)) |
+                         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(live >> 32)) << 32);
+  if (__all(live == wlive)) {
+    uint64_t lv = wlive;
+    while (lv) merge_batch(lv);
+  } else {
+    while (live) merge_batch(live);
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   OT* dst = reinterpret_cast<OT*>(args.o_out) + oi;
