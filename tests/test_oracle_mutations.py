@@ -56,6 +56,23 @@ def _fwd_lse_log2(q, k, v, mask, scale):
 
 
 _ORIG_FWD = O.attention_fwd
+_ORIG_SHARE_BWD = O.share_bwd
+
+
+def _share_bwd_own_swapped(*a, **k):          # own-block dK and dV exchanged
+    dq, dkc, dvc, dkx, dvx = _ORIG_SHARE_BWD(*a, **k)
+    return dq, dkc, dvc, dvx, dkx
+
+
+def _share_bwd_own_rows_rolled(*a, **k):      # own-block rows written one block off
+    dq, dkc, dvc, dkx, dvx = _ORIG_SHARE_BWD(*a, **k)
+    B = a[6]
+    return dq, dkc, dvc, np.roll(dkx, B, axis=1), np.roll(dvx, B, axis=1)
+
+
+def _share_bwd_window_dk_unscaled(*a, **k):   # clean-window dK missing the softmax scale
+    dq, dkc, dvc, dkx, dvx = _ORIG_SHARE_BWD(*a, **k)
+    return dq, dkc / a[13], dvc, dkx, dvx
 
 MUTATIONS = [
     ("_visible", _mask_lt, [P.test_mask_matches_hand_written_fixture, ("mask_L4_B2.txt", 4, 2)]),
@@ -67,6 +84,9 @@ MUTATIONS = [
     ("kv_head_of", _kv_head_mod, [P.test_backward_equals_sdpa_autograd, (16, 4, 4, 2, 8)]),
     ("merge_partials", _merge_no_weights, [P.test_chunked_prefix_merge_equals_single_pass, (16,)]),
     ("attention_fwd", _fwd_lse_log2, [P.test_zero_query_closed_form]),
+    ("share_bwd", _share_bwd_own_swapped, [P.test_share_backward_own_block_equals_full_problem, (16,)]),
+    ("share_bwd", _share_bwd_own_rows_rolled, [P.test_share_backward_own_block_equals_full_problem, (64,)]),
+    ("share_bwd", _share_bwd_window_dk_unscaled, [P.test_share_backward_own_block_equals_full_problem, (16,)]),
 ]
 
 

@@ -427,3 +427,59 @@ def test_sampled_units_equal_full_computation():
     m = O.bdlm_fwd_bwd(x["qc"], x["kc"], x["vc"], x["qx"], x["kx"], x["vx"], doc, dox, B, 0.5)
     np.testing.assert_allclose(dk_s, np.concatenate([m["dkc"], m["dkx"]], 1), atol=1e-13)
     np.testing.assert_allclose(dv_s, np.concatenate([m["dvc"], m["dvx"]], 1), atol=1e-13)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_share_backward_own_block_equals_full_problem(chunk):
+    """The share-mode backward's own-block dK/dV (and its clean windows) equal
+    the full length-2L backward's dK/dV when the local corrupted blocks are
+    scattered into a full problem whose dO is zero everywhere else: only those
+    rows then carry a gradient, so the full dK/dV are exactly their
+    contributions (BP exactness, review Strengths, Prop. 1 / App. A).  The
+    per-block dK/dV are also checked against torch SDPA autograd over each
+    block's keys [clean prefix ; own block], summed over the GQA group."""
+    L, B, hq, hkv, d = 64, 8, 4, 2, 4
+    rng = np.random.default_rng(90 + chunk)
+    ids = np.sort(rng.choice(L // B, size=3, replace=False))
+    T = len(ids) * B
+    kc, vc = _rand(rng, 1, L, hkv, d), _rand(rng, 1, L, hkv, d)
+    qx, kx, vx = _rand(rng, 1, T, hq, d), _rand(rng, 1, T, hkv, d), _rand(rng, 1, T, hkv, d)
+    dox = _rand(rng, 1, T, hq, d)
+    scale = 0.55
+    o_f, lse_f = O.share_fwd(qx, kx, vx, kc, vc, ids, B, 0, L, 1, scale)
+    own = O.share_bwd(qx, kx, vx, kc, vc, ids, B, 0, 0, 1, o_f, lse_f, dox, scale)
+    dkc = np.zeros_like(kc)
+    dvc = np.zeros_like(vc)
+    for j in range(0, L, chunk):
+        e = min(j + chunk, L)
+        r = O.share_bwd(qx, kx, vx, kc, vc, ids, B, j, e, 0, o_f, lse_f, dox, scale)
+        dkc[:, j:e] = r[1]
+        dvc[:, j:e] = r[2]
+    # scatter into a full problem with dO zero outside the local corrupted blocks
+    qc_f = _rand(rng, 1, L, hq, d)
+    qx_f, kx_f, vx_f = _rand(rng, 1, L, hq, d), _rand(rng, 1, L, hkv, d), _rand(rng, 1, L, hkv, d)
+    dox_f = np.zeros((1, L, hq, d))
+    for i, bid in enumerate(ids):
+        src, dst = slice(i * B, (i + 1) * B), slice(bid * B, (bid + 1) * B)
+        qx_f[0, dst], kx_f[0, dst], vx_f[0, dst] = qx[0, src], kx[0, src], vx[0, src]
+        dox_f[0, dst] = dox[0, src]
+    full = O.bdlm_fwd_bwd(qc_f, kc, vc, qx_f, kx_f, vx_f, np.zeros_like(qc_f), dox_f, B, scale)
+    for i, bid in enumerate(ids):
+        src, dst = slice(i * B, (i + 1) * B), slice(bid * B, (bid + 1) * B)
+        np.testing.assert_allclose(own[3][0, src], full["dkx"][0, dst], atol=1e-13, err_msg="dkx")
+        np.testing.assert_allclose(own[4][0, src], full["dvx"][0, dst], atol=1e-13, err_msg="dvx")
+    np.testing.assert_allclose(dkc, full["dkc"], atol=1e-13, err_msg="dkc")
+    np.testing.assert_allclose(dvc, full["dvc"], atol=1e-13, err_msg="dvc")
+    # SDPA autograd per (block, head): dK/dV over [clean prefix ; own block]
+    rep = hq // hkv
+    for i, bid in enumerate(ids):
+        r = slice(i * B, (i + 1) * B)
+        for g in range(hkv):
+            kt = torch.tensor(np.concatenate([kc[0, :bid * B, g], kx[0, r, g]]), requires_grad=True)
+            vt = torch.tensor(np.concatenate([vc[0, :bid * B, g], vx[0, r, g]]), requires_grad=True)
+            for h in range(g * rep, (g + 1) * rep):
+                o = torch.nn.functional.scaled_dot_product_attention(
+                    torch.tensor(qx[0, r, h])[None], kt[None], vt[None], scale=scale)[0]
+                (o * torch.tensor(dox[0, r, h])).sum().backward()
+            np.testing.assert_allclose(own[3][0, r, g], kt.grad.numpy()[bid * B:], atol=1e-12)
+            np.testing.assert_allclose(own[4][0, r, g], vt.grad.numpy()[bid * B:], atol=1e-12)
