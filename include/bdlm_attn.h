@@ -31,9 +31,12 @@
  *     dense row-major.  Q/K/V/O/dO/dQ/dK/dV use [batch, tokens, heads, head_dim];
  *     LSE uses [batch, Hq, tokens] fp32.
  *   - Element type is desc->dtype (BDLM_F32 or BDLM_BF16) unless stated fp32.
- *   - Calls are asynchronous on `stream` (0 = the null stream).  Every argument is
- *     validated before anything is enqueued; on error the call returns a non-zero
- *     bdlm_status, enqueues nothing and leaves all outputs untouched.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  Every argument and
+ *     every launch size is validated before anything is enqueued; on such an error
+ *     the call returns a non-zero bdlm_status, enqueues nothing and leaves all
+ *     outputs untouched.  BDLM_ERR_HIP (the runtime refusing a launch) is the one
+ *     exception: a call that launches several kernels (bdlm_attn_bwd) may then
+ *     have enqueued the launches before the refused one.
  *   - No call allocates device memory.  Scratch memory is the caller's `ws`
  *     buffer of at least bdlm_attn_workspace_bytes() bytes, which must stay
  *     alive, and not be shared with a concurrent call, until the stream reaches
@@ -142,7 +145,15 @@ int bdlm_attn_fwd(const bdlm_attn_desc* desc,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Backward with the stored-LSE recompute (P is rebuilt from Q, K and LSE):
+ * Backward of bdlm_attn_fwd.  The gradients are those of the length-2L masked
+ * attention over [x0 ; xt]; in share mode they are the block-separated terms
+ * whose sum over the streamed clean chunks (and the own block) equals it up to
+ * floating-point reduction order: the objective separates over target blocks,
+ * so a corrupted block's gradients can be formed on one rank against the clean
+ * prefix, and the clean K/V gradients of a chunk are what CSBP returns to the
+ * chunk's owner (pages: review Strengths, Prop. 1 / App. A, exactness of BP;
+ * FAQ "What is CSBP?", only clean K/V and their gradients are exchanged).
+ * Stored-LSE recompute (P is rebuilt from Q, K and LSE):
  * D = rowsum(dO * O) (with LSE * log2(e), kept in the workspace: fp32
  * [batch, Hq, rows] each, per query stream), then dK/dV key-major and dQ
  * query-major (no atomics).
@@ -169,8 +180,11 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Merge attention partials over disjoint key sets (the online (O, LSE) merge of
- * CSBP's streamed clean prefix):
+ * Merge attention partials over disjoint key sets: the (O, LSE) combination by
+ * which a corrupted block's attention over the clean prefix, streamed in chunks
+ * under CSBP, is assembled from one partial per chunk; exact up to
+ * floating-point reduction order (pages: review FAQ "What is CSBP?", the clean
+ * sequence sharded and only clean K/V exchanged; Strengths, Prop. 1 / App. A):
  *   LSE = log sum_j exp(LSE_j),  O = sum_j exp(LSE_j - LSE) O_j.
  * o_parts, lse_parts: HOST arrays of num_parts (1..BDLM_MAX_MERGE_PARTS) DEVICE
  * pointers; O_j fp32 [batch, tokens, heads, head_dim], LSE_j fp32

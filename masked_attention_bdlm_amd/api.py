@@ -53,12 +53,108 @@ def desc_for(q: torch.Tensor, k: torch.Tensor, block: int, scale: Optional[float
                      kv_begin, kv_end, own_block, clean_queries, accumulate)
 
 
+# ------------------------------------------------------------ argument checks
+# The C ABI takes raw pointers and derives every size from the descriptor, so a
+# tensor of the wrong dtype or shape would be read or written out of bounds.
+# These checks run on the host before any pointer is passed on.
+_TORCH_OF = {BDLM_BF16: torch.bfloat16, BDLM_F32: torch.float32}
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtype, device=None, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device} (all tensors on one device)")
+
+
+def _forbid(**named):
+    for k, v in named.items():
+        if v is not None:
+            raise ValueError(f"{k} must be None in share mode")
+
+
+def _shapes(desc):
+    b, L, hq, hkv, d = desc.batch, desc.seqlen, desc.num_q_heads, desc.num_kv_heads, desc.head_dim
+    rows = L if desc.num_local_blocks == 0 else desc.num_local_blocks * desc.block
+    return (b, rows, hq, d), (b, L, hkv, d), (b, rows, hkv, d), (b, hq, rows)
+
+
+def check_fwd_args(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x):
+    """Shapes, dtypes and device of a bdlm_attn_fwd call against `desc`."""
+    dt = _TORCH_OF.get(desc.dtype)
+    if dt is None:
+        raise ValueError(f"descriptor dtype {desc.dtype} is not BDLM_F32 or BDLM_BF16")
+    qs, kcs, kxs, ls = _shapes(desc)
+    dev = qx.device if qx is not None else None
+    _expect(qx, "qx", qs, dt, dev)
+    _expect(kc, "kc", kcs, dt, dev)
+    _expect(vc, "vc", kcs, dt, dev)
+    if desc.num_local_blocks == 0:
+        for n, t, shp in (("qc", qc, qs), ("kx", kx, kxs), ("vx", vx, kxs), ("oc", oc, qs), ("ox", ox, qs)):
+            _expect(t, n, shp, dt, dev)
+        _expect(lse_c, "lse_c", ls, torch.float32, dev)
+    else:
+        _forbid(qc=qc, oc=oc, lse_c=lse_c)
+        opt = not desc.own_block
+        _expect(kx, "kx", kxs, dt, dev, optional=opt)
+        _expect(vx, "vx", kxs, dt, dev, optional=opt)
+        _expect(ox, "ox (share-mode partial, fp32)", qs, torch.float32, dev)
+    _expect(lse_x, "lse_x", ls, torch.float32, dev)
+
+
+def check_bwd_args(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox,
+                   dqc, dkc, dvc, dqx, dkx, dvx):
+    """Shapes, dtypes and device of a bdlm_attn_bwd call against `desc`."""
+    dt = _TORCH_OF.get(desc.dtype)
+    if dt is None:
+        raise ValueError(f"descriptor dtype {desc.dtype} is not BDLM_F32 or BDLM_BF16")
+    qs, kcs, kxs, ls = _shapes(desc)
+    dev = qx.device if qx is not None else None
+    for n, t, shp in (("qx", qx, qs), ("kc", kc, kcs), ("vc", vc, kcs), ("ox", ox, qs), ("dox", dox, qs),
+                      ("dkc", dkc, kcs), ("dvc", dvc, kcs)):
+        _expect(t, n, shp, dt, dev)
+    _expect(lse_x, "lse_x", ls, torch.float32, dev)
+    if desc.num_local_blocks == 0:
+        for n, t, shp in (("qc", qc, qs), ("kx", kx, kxs), ("vx", vx, kxs), ("oc", oc, qs), ("doc", doc, qs),
+                          ("dqc", dqc, qs), ("dqx", dqx, qs), ("dkx", dkx, kxs), ("dvx", dvx, kxs)):
+            _expect(t, n, shp, dt, dev)
+        _expect(lse_c, "lse_c", ls, torch.float32, dev)
+    else:
+        _forbid(qc=qc, oc=oc, lse_c=lse_c, doc=doc, dqc=dqc)
+        _expect(dqx, "dqx (share-mode accumulator, fp32)", qs, torch.float32, dev)
+        opt = not desc.own_block
+        for n, t in (("kx", kx), ("vx", vx), ("dkx", dkx), ("dvx", dvx)):
+            _expect(t, n, kxs, dt, dev, optional=opt)
+
+
+def check_merge_args(o_parts, lse_parts, o_out, lse_out):
+    """All partials fp32 of one shape [b, T, H, d] / [b, H, T] on one device."""
+    if len(o_parts) != len(lse_parts) or len(o_parts) == 0:
+        raise ValueError("need the same positive number of O and LSE partials")
+    b, T, H, d = o_parts[0].shape
+    dev = o_parts[0].device
+    for j, (o, l) in enumerate(zip(o_parts, lse_parts)):
+        _expect(o, f"o_parts[{j}]", (b, T, H, d), torch.float32, dev)
+        _expect(l, f"lse_parts[{j}]", (b, H, T), torch.float32, dev)
+    if o_out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"o_out: dtype {o_out.dtype}, expected float32 or bfloat16")
+    _expect(o_out, "o_out", (b, T, H, d), o_out.dtype, dev)
+    _expect(lse_out, "lse_out", (b, H, T), torch.float32, dev)
+
+
 # ---------------------------------------------------------------- C-ABI calls
 def bdlm_attn_workspace_bytes(desc, for_bwd: bool) -> int:
     return int(load().bdlm_attn_workspace_bytes(ctypes.byref(desc), int(bool(for_bwd))))
 
 
 def bdlm_attn_fwd(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, ws=None, stream=None):
+    check_fwd_args(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x)
     ref = qx
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     st = load().bdlm_attn_fwd(ctypes.byref(desc), _ptr(qc), _ptr(kc), _ptr(vc), _ptr(qx), _ptr(kx),
@@ -69,6 +165,7 @@ def bdlm_attn_fwd(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, ws=None, s
 
 def bdlm_attn_bwd(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox,
                   dqc, dkc, dvc, dqx, dkx, dvx, ws=None, stream=None):
+    check_bwd_args(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox, dqc, dkc, dvc, dqx, dkx, dvx)
     ref = qx
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     st = load().bdlm_attn_bwd(ctypes.byref(desc), _ptr(qc), _ptr(kc), _ptr(vc), _ptr(qx), _ptr(kx),
@@ -80,9 +177,8 @@ def bdlm_attn_bwd(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox,
 
 def bdlm_attn_merge_partials(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor],
                              o_out: torch.Tensor, lse_out: torch.Tensor, stream=None):
+    check_merge_args(o_parts, lse_parts, o_out, lse_out)
     n = len(o_parts)
-    if n != len(lse_parts) or n == 0:
-        raise ValueError("need the same positive number of O and LSE partials")
     b, T, H, d = o_parts[0].shape
     op = (ctypes.c_void_p * n)(*[_ptr(t).value for t in o_parts])
     lp = (ctypes.c_void_p * n)(*[_ptr(t).value for t in lse_parts])

@@ -242,80 +242,82 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   const float* lses[2] = {lse_c, lse_x};
   const int nbg = p.batch * p.hkv;
 
+  // Every launch's arguments and grid are built and checked before the first
+  // launch, so an unsupported size enqueues nothing.
   // 1) D = rowsum(dO * O) and LSE * log2(e)
   const void* os[2] = {oc, ox};
   const void* dos[2] = {doc, dox};
+  BwdPreArgs pre[2];
   for (int s = share ? 1 : 0; s < 2; ++s) {
-    BwdPreArgs pa;
+    BwdPreArgs& pa = pre[s];
     pa.batch = p.batch; pa.rows = p.rows[s]; pa.hq = p.hq; pa.D = p.D; pa.stream = s;
     pa.o = os[s]; pa.dout = dos[s]; pa.delta = delta[s];
     pa.lse = lses[s]; pa.lse2 = lse2[s];
-    ProfScope ps("bdlm_bwd_pre", stream);
-    if (launch_bwd_pre(pa, bf, stream) != hipSuccess) return BDLM_ERR_HIP;
   }
-
   // 2) dK, dV: key-major
-  {
-    BwdArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.p = p;
-    a.q[0] = qc; a.q[1] = qx;
-    a.k[0] = kc; a.k[1] = kx;
-    a.v[0] = vc; a.v[1] = vx;
-    a.dout[0] = doc; a.dout[1] = dox;
-    a.lse2[0] = lse2[0]; a.lse2[1] = lse2[1];
-    a.delta[0] = delta[0]; a.delta[1] = delta[1];
-    a.dk[0] = dkc; a.dk[1] = dkx;
-    a.dv[0] = dvc; a.dv[1] = dvx;
-    a.scale = desc->softmax_scale;
-    a.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
-    a.ns0 = share ? 1 : 0;
-    if (share) {
-      a.kbase[0] = p.kv_begin; a.kend[0] = p.kv_end;
-      a.nkt[0] = (p.kv_end - p.kv_begin + kBwdTileN - 1) / kBwdTileN;
-      a.kbase[1] = 0; a.kend[1] = p.klen[1];
-      a.nkt[1] = p.own_block ? (p.klen[1] + kBwdTileN - 1) / kBwdTileN : 0;
-    } else {
-      for (int k = 0; k < 2; ++k) {
-        a.kbase[k] = 0; a.kend[k] = p.L;
-        a.nkt[k] = (p.L + kBwdTileN - 1) / kBwdTileN;
-      }
-    }
-    const int per_bg = a.nkt[0] + a.nkt[1];
-    a.map = make_map(nbg, per_bg);
-    const int64_t grid = (int64_t)nbg * per_bg;
-    if (grid > 0x7fffffff) return BDLM_ERR_UNSUPPORTED;
-    if (grid > 0) {
-      ProfScope ps("bdlm_dkdv", stream);
-      if (launch_dkdv(a, (int)grid, bf, stream) != hipSuccess) return BDLM_ERR_HIP;
+  BwdArgs ka;
+  std::memset(&ka, 0, sizeof(ka));
+  ka.p = p;
+  ka.q[0] = qc; ka.q[1] = qx;
+  ka.k[0] = kc; ka.k[1] = kx;
+  ka.v[0] = vc; ka.v[1] = vx;
+  ka.dout[0] = doc; ka.dout[1] = dox;
+  ka.lse2[0] = lse2[0]; ka.lse2[1] = lse2[1];
+  ka.delta[0] = delta[0]; ka.delta[1] = delta[1];
+  ka.dk[0] = dkc; ka.dk[1] = dkx;
+  ka.dv[0] = dvc; ka.dv[1] = dvx;
+  ka.scale = desc->softmax_scale;
+  ka.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
+  ka.ns0 = share ? 1 : 0;
+  if (share) {
+    ka.kbase[0] = p.kv_begin; ka.kend[0] = p.kv_end;
+    ka.nkt[0] = (p.kv_end - p.kv_begin + kBwdTileN - 1) / kBwdTileN;
+    ka.kbase[1] = 0; ka.kend[1] = p.klen[1];
+    ka.nkt[1] = p.own_block ? (p.klen[1] + kBwdTileN - 1) / kBwdTileN : 0;
+  } else {
+    for (int k = 0; k < 2; ++k) {
+      ka.kbase[k] = 0; ka.kend[k] = p.L;
+      ka.nkt[k] = (p.L + kBwdTileN - 1) / kBwdTileN;
     }
   }
-
+  ka.map = make_map(nbg, ka.nkt[0] + ka.nkt[1]);
+  const int64_t kgrid = (int64_t)nbg * (ka.nkt[0] + ka.nkt[1]);
   // 3) dQ: query-major, no atomics (share mode adds into the fp32 dqx)
-  {
-    DqArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.p = p;
-    a.q[0] = qc; a.q[1] = qx;
-    a.k[0] = kc; a.k[1] = kx;
-    a.v[0] = vc; a.v[1] = vx;
-    a.dout[0] = doc; a.dout[1] = dox;
-    a.lse2[0] = lse2[0]; a.lse2[1] = lse2[1];
-    a.delta[0] = delta[0]; a.delta[1] = delta[1];
-    a.dq[0] = dqc; a.dq[1] = dqx;
-    a.scale = desc->softmax_scale;
-    a.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
-    a.ns0 = share ? 1 : 0;
-    for (int s = 0; s < 2; ++s) a.nqt[s] = (p.rows[s] + kFwdTileM - 1) / kFwdTileM;
-    const int nstr = 2 - a.ns0;
-    const int per_bg = a.nqt[1] * nstr * p.group;
-    a.map = make_map(nbg, per_bg);
-    const int64_t grid = (int64_t)nbg * per_bg;
-    if (grid > 0x7fffffff) return BDLM_ERR_UNSUPPORTED;
-    if (grid > 0) {
-      ProfScope ps("bdlm_dq", stream);
-      if (launch_dq(a, (int)grid, bf, share ? 1 : 0, stream) != hipSuccess) return BDLM_ERR_HIP;
-    }
+  DqArgs qa;
+  std::memset(&qa, 0, sizeof(qa));
+  qa.p = p;
+  qa.q[0] = qc; qa.q[1] = qx;
+  qa.k[0] = kc; qa.k[1] = kx;
+  qa.v[0] = vc; qa.v[1] = vx;
+  qa.dout[0] = doc; qa.dout[1] = dox;
+  qa.lse2[0] = lse2[0]; qa.lse2[1] = lse2[1];
+  qa.delta[0] = delta[0]; qa.delta[1] = delta[1];
+  qa.dq[0] = dqc; qa.dq[1] = dqx;
+  qa.scale = desc->softmax_scale;
+  qa.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
+  qa.ns0 = share ? 1 : 0;
+  for (int s = 0; s < 2; ++s) qa.nqt[s] = (p.rows[s] + kFwdTileM - 1) / kFwdTileM;
+  const int qper_bg = qa.nqt[1] * (2 - qa.ns0) * p.group;
+  qa.map = make_map(nbg, qper_bg);
+  const int64_t qgrid = (int64_t)nbg * qper_bg;
+  if (kgrid > 0x7fffffff || qgrid > 0x7fffffff) return BDLM_ERR_UNSUPPORTED;
+  for (int s = share ? 1 : 0; s < 2; ++s) {
+    const int64_t threads = (int64_t)pre[s].batch * pre[s].rows * pre[s].hq * (pre[s].D / (bf ? 8 : 4));
+    if ((threads + 255) / 256 > 0x7fffffff) return BDLM_ERR_UNSUPPORTED;
+  }
+
+  // From here on a HIP launch error leaves the launches before it enqueued.
+  for (int s = share ? 1 : 0; s < 2; ++s) {
+    ProfScope ps("bdlm_bwd_pre", stream);
+    if (launch_bwd_pre(pre[s], bf, stream) != hipSuccess) return BDLM_ERR_HIP;
+  }
+  if (kgrid > 0) {
+    ProfScope ps("bdlm_dkdv", stream);
+    if (launch_dkdv(ka, (int)kgrid, bf, stream) != hipSuccess) return BDLM_ERR_HIP;
+  }
+  if (qgrid > 0) {
+    ProfScope ps("bdlm_dq", stream);
+    if (launch_dq(qa, (int)qgrid, bf, share ? 1 : 0, stream) != hipSuccess) return BDLM_ERR_HIP;
   }
   return BDLM_OK;
 }

@@ -11,15 +11,16 @@
 // load.  Only key tiles inside a row's visible ranges are visited; tiles on a
 // range edge test each element against [lo, hi).
 //
-// Backward (stored-LSE recompute, "dK/dV accumulated per key tile"): one
-// workgroup per (batch, kv-head, key array, 128-key tile); wave w owns 32 keys
-// and keeps K_w, V_w and its dK_w, dV_w accumulators in registers while it loops
-// over the visible query tiles of every q head of the GQA group.  S and dP are
-// computed with the query as MFMA row, so P and dS (lane = key) are directly the
-// A operands of dV += P^T dO and dK += dS^T Q, whose dO / Q operands are read
-// transposed out of the row-major (double-buffered) LDS tiles.  dS goes
-// through LDS once more for dQ = dS K, which is added into an fp32 accumulator
-// with hardware float atomics, lanes along head_dim.
+// Backward (stored-LSE recompute, "dK/dV accumulated per key tile"), two
+// kernels after a row pass that forms D = rowsum(dO * O) and LSE * log2(e):
+//  - dK/dV, key-major: one workgroup per (batch, kv-head, key array, 128-key
+//    tile); each key's K, V and dK, dV accumulators stay in registers while
+//    the workgroup sweeps the visible query tiles of every q head of the GQA
+//    group.  Producer waves compute S, dP, P and dS; consumer waves accumulate
+//    dV += P^T dO and dK += dS^T Q with dO / Q read transposed out of LDS.
+//  - dQ, query-major (the forward's decomposition): per key tile it recomputes
+//    S^T and dP^T and accumulates dQ^T += K^T dS^T in registers.
+// Every output element is written once by one lane: no atomics.
 
 #include <hip/hip_runtime.h>
 
@@ -365,8 +366,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
   }
 }
 
-// ========================================================== backward: D and zero
-// delta[s][b][h][r] = <dO, O> over head_dim; zero the fp32 dQ accumulator rows.
+// ============================================================ backward: D
+// delta[b][h][r] = <dO, O> over head_dim, and lse2[b][h][r] = LSE * log2(e).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs args) {
   constexpr int VEC = Elt<T>::VEC;

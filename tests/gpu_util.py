@@ -117,3 +117,30 @@ def mask_dout(x, units, offs, block):
         src, dst = (x["doc"], doc) if st == 0 else (x["dox"], dox)
         dst[b, rows, h] = src[b, rows, h]
     return doc, dox
+
+
+def run_parallel(jobs, fn, consume, workers=None):
+    """Run fn(job) for every job on a thread pool (numpy releases the GIL in its
+    array loops; BLAS is held to one thread per worker) and hand each result to
+    consume(job, result) in the calling thread as it completes, so that only a
+    bounded number of large results are alive at once."""
+    import os
+    from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
+
+    from threadpoolctl import threadpool_limits
+
+    workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    jobs = list(jobs)
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        pending = {}
+        it = iter(jobs)
+        for job in it:
+            pending[ex.submit(fn, job)] = job
+            if len(pending) >= 2 * workers:
+                done, _ = wait(pending, return_when=FIRST_COMPLETED)
+                for f in done:
+                    consume(pending.pop(f), f.result())
+        while pending:
+            done, _ = wait(pending, return_when=FIRST_COMPLETED)
+            for f in done:
+                consume(pending.pop(f), f.result())

@@ -214,3 +214,63 @@ def test_rank_layouts_partition_and_balance():
     assert max(c) == sum(range(241, 257)) == 3976              # the last rank: 1.934 x the mean 2056
     # the workload generator draws the same zigzag shard
     assert list(clean_shard_ids(nb, R, 3)) == csbp.rank_blocks(nb, R, 3)
+
+
+def _cpu_full_args(dtype=None, L=64, B=16, hq=4, hkv=2, d=64):
+    import torch
+    dt = dtype or torch.bfloat16
+    q = lambda: torch.zeros((1, L, hq, d), dtype=dt)
+    k = lambda: torch.zeros((1, L, hkv, d), dtype=dt)
+    lse = lambda: torch.zeros((1, hq, L), dtype=torch.float32)
+    desc = M.desc_for(q(), k(), B)
+    return desc, dict(qc=q(), kc=k(), vc=k(), qx=q(), kx=k(), vx=k(), oc=q(), ox=q(), lse_c=lse(), lse_x=lse())
+
+
+def test_binding_rejects_wrong_dtype_shape_and_host_tensors():
+    """The torch binding checks every tensor against the descriptor before a
+    pointer reaches the C ABI: a bf16 buffer where the kernels write fp32 (or a
+    short one) would otherwise be written out of bounds.  CPU tensors with the
+    right shapes pass these checks and are then refused for not being on the GPU."""
+    import torch
+    from masked_attention_bdlm_amd import api
+    desc, a = _cpu_full_args()
+    api.check_fwd_args(desc, **a)
+    for name, bad in (("lse_x", torch.zeros((1, 4, 64), dtype=torch.bfloat16)),
+                      ("ox", torch.zeros((1, 64, 4, 64), dtype=torch.float32)),
+                      ("kx", torch.zeros((1, 64, 4, 64), dtype=torch.bfloat16)),
+                      ("qc", torch.zeros((1, 48, 4, 64), dtype=torch.bfloat16))):
+        b = dict(a, **{name: bad})
+        with pytest.raises(ValueError, match=name):
+            api.check_fwd_args(desc, **b)
+    with pytest.raises(ValueError, match="GPU"):
+        M.bdlm_attn_fwd(desc, *a.values())
+    # backward: full mode gradients in the input dtype
+    g = dict(doc=a["qc"], dox=a["qx"], dqc=a["qc"].clone(), dkc=a["kc"].clone(), dvc=a["kc"].clone(),
+             dqx=a["qx"].clone(), dkx=a["kx"].clone(), dvx=a["kx"].clone())
+    api.check_bwd_args(desc, **a, **g)
+    with pytest.raises(ValueError, match="dkx"):
+        api.check_bwd_args(desc, **a, **dict(g, dkx=torch.zeros((1, 64, 2, 64), dtype=torch.float32)))
+    # share mode: the partial O and the dQ accumulator must be fp32
+    sd = M.desc_for(a["qx"][:, :32], a["kc"], 16, block_ids=[1, 3], kv_begin=0, kv_end=64, own_block=1)
+    s = dict(qc=None, kc=a["kc"], vc=a["vc"], qx=a["qx"][:, :32], kx=a["kx"][:, :32], vx=a["vx"][:, :32],
+             oc=None, ox=torch.zeros((1, 32, 4, 64), dtype=torch.float32), lse_c=None,
+             lse_x=torch.zeros((1, 4, 32), dtype=torch.float32))
+    api.check_fwd_args(sd, **s)
+    with pytest.raises(ValueError, match="ox"):
+        api.check_fwd_args(sd, **dict(s, ox=torch.zeros((1, 32, 4, 64), dtype=torch.bfloat16)))
+    sb = dict(s, ox=torch.zeros((1, 32, 4, 64), dtype=torch.bfloat16), doc=None,
+              dox=torch.zeros((1, 32, 4, 64), dtype=torch.bfloat16), dqc=None, dkc=a["kc"], dvc=a["vc"],
+              dqx=torch.zeros((1, 32, 4, 64), dtype=torch.float32), dkx=s["kx"], dvx=s["vx"])
+    api.check_bwd_args(sd, **sb)
+    with pytest.raises(ValueError, match="dqx"):
+        api.check_bwd_args(sd, **dict(sb, dqx=torch.zeros((1, 32, 4, 64), dtype=torch.bfloat16)))
+    with pytest.raises(ValueError, match="qc"):
+        api.check_fwd_args(sd, **dict(s, qc=a["qc"]))
+    # merge: fp32 partials of one shape
+    o = [torch.zeros((1, 8, 2, 64)) for _ in range(2)]
+    lse = [torch.zeros((1, 2, 8)) for _ in range(2)]
+    api.check_merge_args(o, lse, torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16), torch.zeros((1, 2, 8)))
+    with pytest.raises(ValueError, match="o_parts"):
+        api.check_merge_args([o[0], o[1].bfloat16()], lse, o[0], lse[0])
+    with pytest.raises(ValueError, match="lse_out"):
+        api.check_merge_args(o, lse, o[0], torch.zeros((1, 2, 9)))
