@@ -101,6 +101,15 @@ typedef struct {
      kernel's epilogue); 0 = overwrite them with this call's partial.  Must be 0
      in full mode. */
   int32_t accumulate;
+  /* Share mode only: 1 = kc, vc (and in the backward dkc, dvc) hold just this
+     call's window, rows [kv_begin, kv_end) of the clean sequence, as
+     [batch, kv_end - kv_begin, Hkv, d]: a chunk-sized staging buffer, the way a
+     rank receives a shard of the clean K/V from an all-gather and hands the
+     chunk's clean dK/dV to a reduce-scatter (pages: review FAQ "What is CSBP?",
+     the clean sequence sharded and only clean K/V and their gradients
+     exchanged).  0 = they hold the whole clean sequence [batch, L, Hkv, d].
+     Must be 0 in full mode. */
+  int32_t kv_staged;
 } bdlm_attn_desc;
 
 /* Bytes of scratch memory a call needs (0 is possible).  for_bwd selects

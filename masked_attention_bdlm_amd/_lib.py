@@ -34,6 +34,7 @@ class BdlmDesc(ctypes.Structure):
         ("num_local_blocks", ctypes.c_int32), ("block_ids", ctypes.POINTER(ctypes.c_int32)),
         ("kv_begin", ctypes.c_int32), ("kv_end", ctypes.c_int32), ("own_block", ctypes.c_int32),
         ("clean_queries", ctypes.c_int32), ("accumulate", ctypes.c_int32),
+        ("kv_staged", ctypes.c_int32),
     ]
 
 
@@ -96,7 +97,7 @@ def check(fn: str, status: int) -> None:
 
 
 def make_desc(batch, seqlen, block, hq, hkv, head_dim, dtype, scale, block_ids=None,
-              kv_begin=0, kv_end=0, own_block=0, clean_queries=0, accumulate=0):
+              kv_begin=0, kv_end=0, own_block=0, clean_queries=0, accumulate=0, kv_staged=0):
     """Build a descriptor; keeps the host block-id array alive on the object."""
     d = BdlmDesc()
     d.batch, d.seqlen, d.block = int(batch), int(seqlen), int(block)
@@ -111,9 +112,11 @@ def make_desc(batch, seqlen, block, hq, hkv, head_dim, dtype, scale, block_ids=N
         d.kv_begin, d.kv_end, d.own_block = int(kv_begin), int(kv_end), int(own_block)
         d.clean_queries = int(clean_queries)
         d.accumulate = int(accumulate)
+        d.kv_staged = int(kv_staged)
     else:
         d.num_local_blocks = 0
         d.block_ids = None
         d.clean_queries = int(clean_queries)
         d.accumulate = int(accumulate)
+        d.kv_staged = int(kv_staged)
     return d

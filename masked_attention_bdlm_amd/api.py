@@ -25,6 +25,10 @@ def _ptr(t: Optional[torch.Tensor]):
         raise ValueError("tensors must live on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous (row-major [batch, tokens, heads, head_dim])")
+    if t.numel() == 0:
+        # torch reports address 0 for an empty tensor; an empty view (say a
+        # staged window of no rows) still has the address of its storage
+        return ctypes.c_void_p(t.untyped_storage().data_ptr() + t.storage_offset() * t.element_size())
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -42,15 +46,18 @@ def dtype_code(dt: torch.dtype) -> int:
 
 def desc_for(q: torch.Tensor, k: torch.Tensor, block: int, scale: Optional[float] = None,
              seqlen: Optional[int] = None, block_ids=None, kv_begin=0, kv_end=0, own_block=0,
-             clean_queries=0, accumulate=0):
-    """Descriptor from Q [batch, tokens, Hq, d] and K [batch, L, Hkv, d]."""
+             clean_queries=0, accumulate=0, kv_staged=0):
+    """Descriptor from Q [batch, tokens, Hq, d] and K [batch, L, Hkv, d] (with
+    kv_staged, K holds only the window and `seqlen` must be given)."""
     b, _, hq, d = q.shape
     hkv = k.shape[2]
+    if kv_staged and seqlen is None:
+        raise ValueError("a staged window needs the clean sequence length (seqlen)")
     L = seqlen if seqlen is not None else k.shape[1]
     if scale is None:
         scale = d ** -0.5
     return make_desc(b, L, block, hq, hkv, d, dtype_code(q.dtype), scale, block_ids,
-                     kv_begin, kv_end, own_block, clean_queries, accumulate)
+                     kv_begin, kv_end, own_block, clean_queries, accumulate, kv_staged)
 
 
 # ------------------------------------------------------------ argument checks
@@ -82,7 +89,8 @@ def _forbid(**named):
 def _shapes(desc):
     b, L, hq, hkv, d = desc.batch, desc.seqlen, desc.num_q_heads, desc.num_kv_heads, desc.head_dim
     rows = L if desc.num_local_blocks == 0 else desc.num_local_blocks * desc.block
-    return (b, rows, hq, d), (b, L, hkv, d), (b, rows, hkv, d), (b, hq, rows)
+    kvrows = desc.kv_end - desc.kv_begin if (desc.num_local_blocks and desc.kv_staged) else L
+    return (b, rows, hq, d), (b, kvrows, hkv, d), (b, rows, hkv, d), (b, hq, rows)
 
 
 def check_fwd_args(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x):
@@ -219,14 +227,15 @@ def attention_bwd(qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox, block:
 
 def share_fwd(qx, kx, vx, kc, vc, block_ids, block: int, kv_begin: int, kv_end: int,
               own_block: int, scale: Optional[float] = None, out=None, stream=None, clean_queries: int = 0,
-              accumulate: int = 0):
+              accumulate: int = 0, seqlen: Optional[int] = None, kv_staged: int = 0):
     """Share-mode partial over one key window: returns (O_part fp32, LSE_part).
 
     clean_queries=1: qx holds clean query blocks (each sees the clean keys of its
     own and every earlier block); kx, vx may then be None.  accumulate=1: merge
-    the partial into the (O, LSE) already held in `out` instead."""
-    desc = desc_for(qx, kc, block, scale, block_ids=block_ids, kv_begin=kv_begin, kv_end=kv_end,
-                    own_block=own_block, clean_queries=clean_queries, accumulate=accumulate)
+    the partial into the (O, LSE) already held in `out` instead.  kv_staged=1:
+    kc, vc hold only the window's rows (then `seqlen` = L is required)."""
+    desc = desc_for(qx, kc, block, scale, seqlen=seqlen, block_ids=block_ids, kv_begin=kv_begin, kv_end=kv_end,
+                    own_block=own_block, clean_queries=clean_queries, accumulate=accumulate, kv_staged=kv_staged)
     b, T, hq, d = qx.shape
     if out is None:
         o = torch.empty((b, T, hq, d), dtype=torch.float32, device=qx.device)
@@ -240,10 +249,11 @@ def share_fwd(qx, kx, vx, kc, vc, block_ids, block: int, kv_begin: int, kv_end: 
 def share_bwd(qx, kx, vx, kc, vc, block_ids, block: int, kv_begin: int, kv_end: int, own_block: int,
               o_final, lse_final, dox, dqx_acc, dkc, dvc, dkx=None, dvx=None,
               scale: Optional[float] = None, ws: Optional[torch.Tensor] = None, stream=None,
-              clean_queries: int = 0):
-    """Share-mode backward of one key window (adds into dqx_acc, writes the window of dkc/dvc)."""
-    desc = desc_for(qx, kc, block, scale, block_ids=block_ids, kv_begin=kv_begin, kv_end=kv_end,
-                    own_block=own_block, clean_queries=clean_queries)
+              clean_queries: int = 0, seqlen: Optional[int] = None, kv_staged: int = 0):
+    """Share-mode backward of one key window (adds into dqx_acc, writes the window of dkc/dvc;
+    with kv_staged=1, kc/vc/dkc/dvc hold only the window's rows)."""
+    desc = desc_for(qx, kc, block, scale, seqlen=seqlen, block_ids=block_ids, kv_begin=kv_begin, kv_end=kv_end,
+                    own_block=own_block, clean_queries=clean_queries, kv_staged=kv_staged)
     if ws is None:
         ws = workspace(desc, True, qx.device)
     bdlm_attn_bwd(desc, None, kc, vc, qx, kx, vx, None, o_final, None, lse_final, None, dox,

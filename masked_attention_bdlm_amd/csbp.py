@@ -149,6 +149,99 @@ def clean_share_backward(qs, kc, vc, ids: Sequence[int], B: int, chunk: int, o, 
     return bufs.dqx, bufs.dkc, bufs.dvc
 
 
+# ------------------------------------------------- staged clean chunks (bounded)
+class StagedBuffers(ShareBuffers):
+    """Buffers of a share step whose clean K/V never reside whole on the rank:
+    two chunk-sized staging slots for K/V (the one being consumed and the one
+    being received) and two for the chunk's clean dK/dV (the one being written
+    and the one being sent), as an all-gather / reduce-scatter pair would use
+    them.  The local corrupted blocks' buffers are those of ShareBuffers."""
+
+    def __init__(self, qx: torch.Tensor, kx: Optional[torch.Tensor], hkv: int, chunk: int):
+        b, T, hq, d = qx.shape
+        dev, dt = qx.device, qx.dtype
+        shape = (b, chunk, hkv, d)
+        self.k_stage = [torch.empty(shape, dtype=dt, device=dev) for _ in range(2)]
+        self.v_stage = [torch.empty(shape, dtype=dt, device=dev) for _ in range(2)]
+        self.dk_stage = [torch.empty(shape, dtype=dt, device=dev) for _ in range(2)]
+        self.dv_stage = [torch.empty(shape, dtype=dt, device=dev) for _ in range(2)]
+        self.chunk = chunk
+        self.acc_o = torch.empty((b, T, hq, d), dtype=torch.float32, device=dev)
+        self.acc_lse = torch.empty((b, hq, T), dtype=torch.float32, device=dev)
+        self.o = torch.empty_like(qx)
+        self.lse = torch.empty_like(self.acc_lse)
+        self.dqx = torch.empty((b, T, hq, d), dtype=torch.float32, device=dev)
+        self.dkc = self.dvc = None
+        self.dkx = torch.empty_like(kx) if kx is not None else None
+        self.dvx = torch.empty_like(kx) if kx is not None else None
+        self.ws = None
+
+
+def share_forward_staged(qx, kx, vx, L: int, ids: Sequence[int], B: int, chunk: int, fetch,
+                         scale: Optional[float] = None, bufs: Optional[StagedBuffers] = None,
+                         stream=None, clean_queries: int = 0):
+    """share_forward / clean_share_forward with the clean K/V delivered chunk
+    by chunk into a staging slot: fetch(j0, j1, k_dst, v_dst) fills k_dst, v_dst
+    [batch, j1 - j0, Hkv, d] with clean rows [j0, j1) on `stream` (on one GPU
+    a copy stands in for the all-gather's receive).  Returns (O, LSE)."""
+    if qx.shape[0] != 1:
+        raise ValueError("the share step streams one sequence (batch 1)")
+    ids = [int(i) for i in ids]
+    own = 0 if clean_queries else 1
+    wins = _clean_chunks(L, chunk, ids, B) if clean_queries else _chunks(L, chunk, ids, B)
+    first = True
+    if own:
+        ks, vs = bufs.k_stage[0][:, :0], bufs.v_stage[0][:, :0]      # the own-block call reads no clean key
+        d = desc_for(qx, ks, B, scale, seqlen=L, block_ids=ids, kv_begin=0, kv_end=0, own_block=1, kv_staged=1)
+        bdlm_attn_fwd(d, None, ks, vs, qx, kx, vx, None, bufs.acc_o, None, bufs.acc_lse, None, stream)
+        first = False
+    for n, (j0, j1) in enumerate(wins):
+        ks, vs = bufs.k_stage[n % 2][:, :j1 - j0], bufs.v_stage[n % 2][:, :j1 - j0]
+        fetch(j0, j1, ks, vs)
+        d = desc_for(qx, ks, B, scale, seqlen=L, block_ids=ids, kv_begin=j0, kv_end=j1, own_block=0,
+                     clean_queries=clean_queries, accumulate=0 if first else 1, kv_staged=1)
+        bdlm_attn_fwd(d, None, ks, vs, qx, kx if own else None, vx if own else None, None, bufs.acc_o, None,
+                      bufs.acc_lse, None, stream)
+        first = False
+    bdlm_attn_merge_partials([bufs.acc_o], [bufs.acc_lse], bufs.o, bufs.lse, stream)
+    return bufs.o, bufs.lse
+
+
+def share_backward_staged(qx, kx, vx, L: int, ids: Sequence[int], B: int, chunk: int, o, lse, dox, fetch,
+                          deliver, scale: Optional[float] = None, bufs: Optional[StagedBuffers] = None,
+                          stream=None, clean_queries: int = 0):
+    """share_backward / clean_share_backward with staged chunks: each chunk's
+    clean K/V are fetched again (fetch as in share_forward_staged) and its clean
+    dK/dV, written into a staging slot, are handed to deliver(j0, j1, dk, dv)
+    (on one GPU a copy stands in for the reduce-scatter's send).  Returns
+    (dqx fp32, dkx, dvx); dkx, dvx are None for clean query blocks."""
+    ids = [int(i) for i in ids]
+    own = 0 if clean_queries else 1
+    wins = _clean_chunks(L, chunk, ids, B) if clean_queries else _chunks(L, chunk, ids, B)
+    bufs.dqx.zero_()
+    if bufs.ws is None:
+        d_full = desc_for(qx, bufs.k_stage[0], B, scale, seqlen=L, block_ids=ids, kv_begin=0,
+                          kv_end=min(chunk, L), own_block=own, clean_queries=clean_queries, kv_staged=1)
+        bufs.ws = workspace(d_full, True, qx.device)
+    for n, (j0, j1) in enumerate(wins):
+        W = j1 - j0
+        ks, vs = bufs.k_stage[n % 2][:, :W], bufs.v_stage[n % 2][:, :W]
+        dks, dvs = bufs.dk_stage[n % 2][:, :W], bufs.dv_stage[n % 2][:, :W]
+        fetch(j0, j1, ks, vs)
+        d = desc_for(qx, ks, B, scale, seqlen=L, block_ids=ids, kv_begin=j0, kv_end=j1, own_block=0,
+                     clean_queries=clean_queries, kv_staged=1)
+        bdlm_attn_bwd(d, None, ks, vs, qx, kx if own else None, vx if own else None, None, o, None, lse, None,
+                      dox, None, dks, dvs, bufs.dqx, None, None, bufs.ws, stream)
+        deliver(j0, j1, dks, dvs)
+    if own:
+        ks, vs = bufs.k_stage[0][:, :0], bufs.v_stage[0][:, :0]
+        dks, dvs = bufs.dk_stage[0][:, :0], bufs.dv_stage[0][:, :0]
+        d = desc_for(qx, ks, B, scale, seqlen=L, block_ids=ids, kv_begin=0, kv_end=0, own_block=1, kv_staged=1)
+        bdlm_attn_bwd(d, None, ks, vs, qx, kx, vx, None, o, None, lse, None, dox,
+                      None, dks, dvs, bufs.dqx, bufs.dkx, bufs.dvx, bufs.ws, stream)
+    return bufs.dqx, bufs.dkx, bufs.dvx
+
+
 # ------------------------------------------------------------------ rank layout
 def rank_blocks(nblocks: int, nranks: int, rank: int, layout: str = "zigzag") -> List[int]:
     """Blocks a rank owns (its corrupted target blocks and its shard of the

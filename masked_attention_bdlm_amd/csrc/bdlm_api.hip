@@ -75,7 +75,8 @@ int check_desc(const bdlm_attn_desc* d) {
     if (d->clean_queries != 0 && d->clean_queries != 1) return BDLM_ERR_INVALID_ARG;
     if (d->clean_queries && d->own_block) return BDLM_ERR_INVALID_ARG;
     if (d->accumulate != 0 && d->accumulate != 1) return BDLM_ERR_INVALID_ARG;
-  } else if (d->clean_queries != 0 || d->accumulate != 0) {
+    if (d->kv_staged != 0 && d->kv_staged != 1) return BDLM_ERR_INVALID_ARG;
+  } else if (d->clean_queries != 0 || d->accumulate != 0 || d->kv_staged != 0) {
     return BDLM_ERR_INVALID_ARG;
   }
   return BDLM_OK;
@@ -98,7 +99,9 @@ Problem make_problem(const bdlm_attn_desc* d) {
     p.mode = 1;
     p.nlocal = d->num_local_blocks;
     p.rows[0] = 0; p.rows[1] = p.nlocal * p.B;
-    p.klen[0] = p.L; p.klen[1] = p.nlocal * p.B;
+    // a staged window holds only rows [kv_begin, kv_end) per batch
+    p.klen[0] = d->kv_staged ? d->kv_end - d->kv_begin : p.L;
+    p.klen[1] = p.nlocal * p.B;
     p.kv_begin = d->kv_begin; p.kv_end = d->kv_end; p.own_block = d->own_block;
     p.incl = d->clean_queries;
     for (int i = 0; i < p.nlocal; ++i) p.block_ids[i] = d->block_ids[i];
@@ -115,6 +118,16 @@ XcdMap make_map(int nbg, int per_bg) {
 }
 
 size_t elt_size(int dtype) { return dtype == BDLM_BF16 ? 2 : 4; }
+
+// Address that clean-key row 0 would have in a staged window buffer: the
+// kernels index array-0 rows by their clean-sequence position k, and a staged
+// buffer holds row k at k - kv_begin.  Only rows of the window are ever read
+// or written, so no access lands below the buffer.
+template <typename P> P stage_shift(P ptr, const bdlm_attn_desc* d) {
+  if (!ptr || d->num_local_blocks == 0 || !d->kv_staged) return ptr;
+  const uintptr_t row = (uintptr_t)d->num_kv_heads * d->head_dim * elt_size(d->dtype);
+  return reinterpret_cast<P>(reinterpret_cast<uintptr_t>(ptr) - row * (uintptr_t)d->kv_begin);
+}
 
 // Backward workspace: per query stream, D = rowsum(dO * O) and LSE * log2(e),
 // fp32 [batch, Hq, rows] each.
@@ -188,8 +201,8 @@ int bdlm_attn_fwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   std::memset(&a, 0, sizeof(a));
   a.p = make_problem(desc);
   a.q[0] = qc; a.q[1] = qx;
-  a.k[0] = kc; a.k[1] = kx;
-  a.v[0] = vc; a.v[1] = vx;
+  a.k[0] = stage_shift(kc, desc); a.k[1] = kx;
+  a.v[0] = stage_shift(vc, desc); a.v[1] = vx;
   a.o[0] = oc; a.o[1] = ox;
   a.lse[0] = lse_c; a.lse[1] = lse_x;
   a.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
@@ -208,11 +221,19 @@ int bdlm_attn_fwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   return e == hipSuccess ? BDLM_OK : BDLM_ERR_HIP;
 }
 
-int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, const void* vc,
-                  const void* qx, const void* kx, const void* vx, const void* oc, const void* ox,
-                  const float* lse_c, const float* lse_x, const void* doc, const void* dox,
-                  void* dqc, void* dkc, void* dvc, void* dqx, void* dkx, void* dvx,
-                  void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward behind bdlm_attn_bwd.  `ws_of` is
+// called once every argument has been validated, with the workspace size the
+// call needs; it returns the workspace (or NULL with *err set).
+template <typename WsOf>
+int bwd_impl(const bdlm_attn_desc* desc, const void* qc, const void* kc, const void* vc,
+             const void* qx, const void* kx, const void* vx, const void* oc, const void* ox,
+             const float* lse_c, const float* lse_x, const void* doc, const void* dox,
+             void* dqc, void* dkc, void* dvc, void* dqx, void* dkx, void* dvx,
+             WsOf ws_of, hipStream_t stream) {
   int st = check_desc(desc);
   if (st != BDLM_OK) return st;
   const bool share = desc->num_local_blocks > 0;
@@ -232,7 +253,9 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   for (const void* ptr : need2) if (!ptr || !aligned16(ptr)) return BDLM_ERR_INVALID_ARG;
   if (!lse_x || !aligned4(lse_x)) return BDLM_ERR_INVALID_ARG;
   const BwdLayout lay = bwd_layout(desc);
-  if (lay.total > 0 && (!ws || ws_bytes < lay.total || !aligned16(ws))) return BDLM_ERR_WORKSPACE;
+  int ws_err = BDLM_OK;
+  void* ws = ws_of(lay.total, &ws_err);
+  if (ws_err != BDLM_OK) return ws_err;
 
   const int bf = desc->dtype == BDLM_BF16;
   const Problem p = make_problem(desc);
@@ -259,13 +282,13 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   std::memset(&ka, 0, sizeof(ka));
   ka.p = p;
   ka.q[0] = qc; ka.q[1] = qx;
-  ka.k[0] = kc; ka.k[1] = kx;
-  ka.v[0] = vc; ka.v[1] = vx;
+  ka.k[0] = stage_shift(kc, desc); ka.k[1] = kx;
+  ka.v[0] = stage_shift(vc, desc); ka.v[1] = vx;
   ka.dout[0] = doc; ka.dout[1] = dox;
   ka.lse2[0] = lse2[0]; ka.lse2[1] = lse2[1];
   ka.delta[0] = delta[0]; ka.delta[1] = delta[1];
-  ka.dk[0] = dkc; ka.dk[1] = dkx;
-  ka.dv[0] = dvc; ka.dv[1] = dvx;
+  ka.dk[0] = stage_shift(dkc, desc); ka.dk[1] = dkx;
+  ka.dv[0] = stage_shift(dvc, desc); ka.dv[1] = dvx;
   ka.scale = desc->softmax_scale;
   ka.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
   ka.ns0 = share ? 1 : 0;
@@ -287,8 +310,8 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   std::memset(&qa, 0, sizeof(qa));
   qa.p = p;
   qa.q[0] = qc; qa.q[1] = qx;
-  qa.k[0] = kc; qa.k[1] = kx;
-  qa.v[0] = vc; qa.v[1] = vx;
+  qa.k[0] = stage_shift(kc, desc); qa.k[1] = kx;
+  qa.v[0] = stage_shift(vc, desc); qa.v[1] = vx;
   qa.dout[0] = doc; qa.dout[1] = dox;
   qa.lse2[0] = lse2[0]; qa.lse2[1] = lse2[1];
   qa.delta[0] = delta[0]; qa.delta[1] = delta[1];
@@ -320,6 +343,23 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
     if (launch_dq(qa, (int)qgrid, bf, share ? 1 : 0, stream) != hipSuccess) return BDLM_ERR_HIP;
   }
   return BDLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, const void* vc,
+                  const void* qx, const void* kx, const void* vx, const void* oc, const void* ox,
+                  const float* lse_c, const float* lse_x, const void* doc, const void* dox,
+                  void* dqc, void* dkc, void* dvc, void* dqx, void* dkx, void* dvx,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  auto ws_of = [&](size_t need, int* err) -> void* {
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) *err = BDLM_ERR_WORKSPACE;
+    return ws;
+  };
+  return bwd_impl(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox, dqc, dkc, dvc, dqx, dkx, dvx,
+                  ws_of, stream);
 }
 
 int bdlm_attn_merge_partials(int32_t num_parts, int32_t batch, int64_t tokens, int32_t heads,
@@ -355,7 +395,11 @@ int bdlm_attn_schedule_walk(const bdlm_attn_desc* desc, int for_bwd, uint8_t* co
   int st = check_desc(desc);
   if (st != BDLM_OK) return st;
   if (for_bwd < 0 || for_bwd > 2) return BDLM_ERR_INVALID_ARG;
-  const Problem p = make_problem(desc);
+  // the walk reports clean keys by their position in the clean sequence,
+  // whether or not the call's window is staged
+  bdlm_attn_desc unstaged = *desc;
+  unstaged.kv_staged = 0;
+  const Problem p = make_problem(&unstaged);
   const int64_t nrows = (int64_t)p.rows[0] + p.rows[1];
   const int64_t nkeys = (int64_t)p.klen[0] + p.klen[1];
   if (cover && cover_len < nrows * nkeys) return BDLM_ERR_INVALID_ARG;

@@ -344,3 +344,41 @@ def test_csbp_rank_256k_clean_shard_sampled(sharp):
     units = _share_units(len(ids), w.hq, UNITS, w.seed + 200)
     _share_check(w, x, "qs", "dos", ids, units, row_sample(B, ROWS, w.seed + 9), lambda cid: (cid + 1) * B, False,
                  o, lse, dq, dmasked, label)
+
+
+def test_csbp_share_256k_staged_equals_resident():
+    """At full size (16 blocks of 1024, 256K clean tokens, 8192-token chunks)
+    the staged share step (clean K/V received chunk by chunk into two staging
+    slots, clean dK/dV handed off per chunk) is bit-identical to the step that
+    reads the resident clean K/V."""
+    require_gpu()
+    w = WORKLOADS["csbp_share_256k"]
+    announce(w.name + " staged")
+    x = make_share_inputs(w, device="cuda")
+    ids = [int(i) for i in x["block_ids"]]
+    B, L, C = w.block, w.seqlen, w.share_chunk
+    bufs = csbp.ShareBuffers(x["qx"], x["kc"], x["kx"])
+    o, lse = (t.clone() for t in csbp.share_forward(x["qx"], x["kx"], x["vx"], x["kc"], x["vc"], ids, B, C,
+                                                    w.scale, bufs))
+    ref = [t.clone() for t in csbp.share_backward(x["qx"], x["kx"], x["vx"], x["kc"], x["vc"], ids, B, C, o, lse,
+                                                  x["dox"], w.scale, bufs)]
+    del bufs
+    sb = csbp.StagedBuffers(x["qx"], x["kx"], w.hkv, C)
+    dkc, dvc = torch.zeros_like(x["kc"]), torch.zeros_like(x["vc"])
+
+    def fetch(j0, j1, k_dst, v_dst):
+        k_dst.copy_(x["kc"][:, j0:j1])
+        v_dst.copy_(x["vc"][:, j0:j1])
+
+    def deliver(j0, j1, dk, dv):
+        dkc[:, j0:j1].copy_(dk)
+        dvc[:, j0:j1].copy_(dv)
+
+    so, slse = csbp.share_forward_staged(x["qx"], x["kx"], x["vx"], L, ids, B, C, fetch, w.scale, sb)
+    assert torch.equal(so, o) and torch.equal(slse, lse)
+    sdq, sdkx, sdvx = csbp.share_backward_staged(x["qx"], x["kx"], x["vx"], L, ids, B, C, so, slse, x["dox"],
+                                                 fetch, deliver, w.scale, sb)
+    torch.cuda.synchronize()
+    for name, a, b in (("dqx", sdq, ref[0]), ("dkc", dkc, ref[1]), ("dvc", dvc, ref[2]), ("dkx", sdkx, ref[3]),
+                       ("dvx", sdvx, ref[4])):
+        assert torch.equal(a, b), name

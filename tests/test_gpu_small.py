@@ -311,3 +311,76 @@ def test_merge_kernel_many_parts(d, nparts):
         fin = np.isfinite(ref_l)
         assert (np.isneginf(ml_h) == ~fin).all()
         assert np.max(np.abs(ml_h[fin] - ref_l[fin])) <= 1e-5
+
+
+def _staged_io(kc, vc, dkc, dvc):
+    """fetch / deliver callables over resident full clean K/V and gradients:
+    on one GPU a copy stands in for the all-gather receive and the
+    reduce-scatter send of a chunk."""
+    def fetch(j0, j1, k_dst, v_dst):
+        k_dst.copy_(kc[:, j0:j1])
+        v_dst.copy_(vc[:, j0:j1])
+
+    def deliver(j0, j1, dk, dv):
+        dkc[:, j0:j1].copy_(dk)
+        dvc[:, j0:j1].copy_(dv)
+    return fetch, deliver
+
+
+@pytest.mark.parametrize("clean,dtype,L,B,n,chunk", [
+    (False, "bf16", 2048, 128, 4, 384),
+    (False, "f32", 1024, 64, 3, 320),
+    (True, "bf16", 2048, 128, 4, 512),
+    (True, "bf16", 1024, 64, 5, 320),
+])
+def test_staged_chunks_equal_resident_clean_kv(clean, dtype, L, B, n, chunk):
+    """The share step with the clean K/V delivered chunk by chunk into a
+    two-slot staging buffer (kv_staged = 1) gives bit-identical O, LSE, dQ and
+    dK/dV to the step that reads the resident clean K/V, and matches the
+    oracle's one pass."""
+    from masked_attention_bdlm_amd import csbp
+    require_gpu()
+    w = Workload(name="staged", batch=1, seqlen=L, block=B, hq=4, hkv=2, head_dim=128, dtype=dtype, seed=23,
+                 q_std=128 ** -0.5, share_blocks=n, share_chunk=chunk)
+    announce(f"staged chunks clean={clean} {dtype} L={L} B={B} n={n} chunk={chunk}")
+    x = make_share_inputs(w, device="cuda", sharp=True)
+    ids = [int(i) for i in x["block_ids"]]
+    q = x["qx"]
+    kx, vx = (None, None) if clean else (x["kx"], x["vx"])
+    if clean:
+        rb = csbp.ShareBuffers(q, x["kc"])
+        o, lse = csbp.clean_share_forward(q, x["kc"], x["vc"], ids, B, chunk, w.scale, rb)
+        o, lse = o.clone(), lse.clone()
+        dq, dkc, dvc = (t.clone() for t in csbp.clean_share_backward(q, x["kc"], x["vc"], ids, B, chunk, o, lse,
+                                                                     x["dox"], w.scale, rb))
+        dkx = dvx = None
+    else:
+        rb = csbp.ShareBuffers(q, x["kc"], kx)
+        o, lse = csbp.share_forward(q, kx, vx, x["kc"], x["vc"], ids, B, chunk, w.scale, rb)
+        o, lse = o.clone(), lse.clone()
+        dq, dkc, dvc, dkx, dvx = (t.clone() for t in csbp.share_backward(q, kx, vx, x["kc"], x["vc"], ids, B,
+                                                                         chunk, o, lse, x["dox"], w.scale, rb))
+    sb = csbp.StagedBuffers(q, kx, w.hkv, chunk)
+    g_dkc, g_dvc = torch.zeros_like(x["kc"]), torch.zeros_like(x["vc"])
+    fetch, deliver = _staged_io(x["kc"], x["vc"], g_dkc, g_dvc)
+    so, slse = csbp.share_forward_staged(q, kx, vx, L, ids, B, chunk, fetch, w.scale, sb, clean_queries=int(clean))
+    so, slse = so.clone(), slse.clone()
+    sdq, sdkx, sdvx = csbp.share_backward_staged(q, kx, vx, L, ids, B, chunk, so, slse, x["dox"], fetch, deliver,
+                                                 w.scale, sb, clean_queries=int(clean))
+    torch.cuda.synchronize()
+    assert torch.equal(so, o) and torch.equal(slse, lse)
+    assert torch.equal(sdq, dq)
+    assert torch.equal(g_dkc, dkc) and torch.equal(g_dvc, dvc)
+    if not clean:
+        assert torch.equal(sdkx, dkx) and torch.equal(sdvx, dvx)
+    xh = host(x)
+    o_ref, lse_ref = O.share_fwd(xh["qx"], xh["kx"], xh["vx"], xh["kc"], xh["vc"], ids, B, 0, L, 0 if clean else 1,
+                                 w.scale, clean_queries=clean)
+    r = O.share_bwd(xh["qx"], xh["kx"], xh["vx"], xh["kc"], xh["vc"], ids, B, 0, L, 0 if clean else 1, o_ref, lse_ref,
+                    xh["dox"], w.scale, clean_queries=clean)
+    got = dict(ox=so, lse_x=slse, dqx=sdq, dkc=g_dkc, dvc=g_dvc)
+    ref = dict(ox=o_ref, lse_x=lse_ref, dqx=r[0], dkc=r[1], dvc=r[2])
+    if not clean:
+        got.update(dkx=sdkx, dvx=sdvx)
+        ref.update(dkx=r[3], dvx=r[4])
+    check_outputs(host(got), ref, dtype, where="staged share")

@@ -43,7 +43,7 @@ def _ok_desc(**kw):
     return make_desc(base["batch"], base["seqlen"], base["block"], base["hq"], base["hkv"],
                      base["head_dim"], base["dtype"], base["scale"], base.get("block_ids"),
                      base.get("kv_begin", 0), base.get("kv_end", 0), base.get("own_block", 0),
-                     base.get("clean_queries", 0), base.get("accumulate", 0))
+                     base.get("clean_queries", 0), base.get("accumulate", 0), base.get("kv_staged", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -274,3 +274,19 @@ def test_binding_rejects_wrong_dtype_shape_and_host_tensors():
         api.check_merge_args([o[0], o[1].bfloat16()], lse, o[0], lse[0])
     with pytest.raises(ValueError, match="lse_out"):
         api.check_merge_args(o, lse, o[0], torch.zeros((1, 2, 9)))
+
+
+def test_staged_window_descriptor_and_walk():
+    """kv_staged is a share-mode field (0 or 1); the host walk reports the same
+    key coverage whether or not the window is staged (it is only a memory
+    layout of the clean rows)."""
+    lib = M.load()
+    assert lib.bdlm_attn_check_desc(ctypes.byref(_ok_desc(kv_staged=1))) == 1      # full mode
+    sd = dict(block_ids=[1, 4, 6, 12], kv_begin=64, kv_end=160, own_block=0)
+    assert lib.bdlm_attn_check_desc(ctypes.byref(_ok_desc(kv_staged=2, **sd))) == 1
+    assert lib.bdlm_attn_check_desc(ctypes.byref(_ok_desc(kv_staged=1, **sd))) == 0
+    for fb in (0, 1, 2):
+        a, sa = M.schedule_walk(_ok_desc(kv_staged=1, **sd), fb)
+        b, sb_ = M.schedule_walk(_ok_desc(kv_staged=0, **sd), fb)
+        assert (a == b).all() and sa == sb_
+
