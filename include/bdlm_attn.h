@@ -189,6 +189,37 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * bdlm_attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving or training loops,
+ * harnesses that forbid allocation calls).  Same arguments, semantics and
+ * results as bdlm_attn_bwd (the same kernels run), minus ws / ws_bytes: the
+ * workspace is a fixed array of bdlm_attn_noalloc_scratch_bytes() bytes (64 MiB)
+ * that is part of the library's device image, one copy per GPU, held until the
+ * process ends.  The call uses the copy of the CURRENT device (the stream must
+ * belong to it) and allocates nothing.
+ *   - A problem whose workspace (bdlm_attn_workspace_bytes(desc, 1)) exceeds the
+ *     array returns BDLM_ERR_UNSUPPORTED before anything is enqueued.  The
+ *     limit admits batch * Hq * rows <= 4M (query rows of both streams counted
+ *     once: e.g. 32 q heads at L = 131072).
+ *   - Nothing in the array must start at zero: every call writes the parts it
+ *     reads before reading them.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap in
+ *     time (different streams, or the same stream from different threads
+ *     without ordering) race on it and must not be issued.
+ * Returns BDLM_ERR_HIP if the device or the array's address cannot be found.
+ */
+int bdlm_attn_bwd_noalloc(const bdlm_attn_desc* desc,
+                          const void* qc, const void* kc, const void* vc,
+                          const void* qx, const void* kx, const void* vx,
+                          const void* oc, const void* ox, const float* lse_c, const float* lse_x,
+                          const void* doc, const void* dox,
+                          void* dqc, void* dkc, void* dvc, void* dqx, void* dkx, void* dvx,
+                          hipStream_t stream);
+
+/* Size in bytes of the per-GPU workspace array of bdlm_attn_bwd_noalloc. */
+size_t bdlm_attn_noalloc_scratch_bytes(void);
+
+/*
  * Merge attention partials over disjoint key sets: the (O, LSE) combination by
  * which a corrupted block's attention over the clean prefix, streamed in chunks
  * under CSBP, is assembled from one partial per chunk; exact up to

@@ -23,6 +23,7 @@ EXPORTED = (
     "bdlm_attn_workspace_bytes", "bdlm_attn_check_desc", "bdlm_attn_fwd", "bdlm_attn_bwd",
     "bdlm_attn_merge_partials", "bdlm_attn_schedule_walk", "bdlm_status_str",
     "bdlm_attn_version", "bdlm_attn_profile_begin", "bdlm_attn_profile_end",
+    "bdlm_attn_bwd_noalloc", "bdlm_attn_noalloc_scratch_bytes",
 )
 
 
@@ -70,6 +71,10 @@ def load() -> ctypes.CDLL:
     lib.bdlm_attn_fwd.restype = ctypes.c_int
     lib.bdlm_attn_bwd.argtypes = [dp] + [vp] * 18 + [vp, sz, vp]
     lib.bdlm_attn_bwd.restype = ctypes.c_int
+    lib.bdlm_attn_bwd_noalloc.argtypes = [dp] + [vp] * 18 + [vp]
+    lib.bdlm_attn_bwd_noalloc.restype = ctypes.c_int
+    lib.bdlm_attn_noalloc_scratch_bytes.argtypes = []
+    lib.bdlm_attn_noalloc_scratch_bytes.restype = sz
     lib.bdlm_attn_merge_partials.argtypes = [i32, i32, i64, i32, i32, ctypes.POINTER(vp),
                                              ctypes.POINTER(vp), vp, i32, vp, vp]
     lib.bdlm_attn_merge_partials.restype = ctypes.c_int

@@ -183,6 +183,18 @@ def bdlm_attn_bwd(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox,
     check("bdlm_attn_bwd", st)
 
 
+def bdlm_attn_bwd_noalloc(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox,
+                          dqc, dkc, dvc, dqx, dkx, dvx, stream=None):
+    """bdlm_attn_bwd with the library's fixed per-GPU workspace array (no
+    workspace argument, nothing allocated)."""
+    check_bwd_args(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox, dqc, dkc, dvc, dqx, dkx, dvx)
+    st = load().bdlm_attn_bwd_noalloc(ctypes.byref(desc), _ptr(qc), _ptr(kc), _ptr(vc), _ptr(qx), _ptr(kx),
+                                      _ptr(vx), _ptr(oc), _ptr(ox), _ptr(lse_c), _ptr(lse_x), _ptr(doc),
+                                      _ptr(dox), _ptr(dqc), _ptr(dkc), _ptr(dvc), _ptr(dqx), _ptr(dkx),
+                                      _ptr(dvx), _stream(stream, qx))
+    check("bdlm_attn_bwd_noalloc", st)
+
+
 def bdlm_attn_merge_partials(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor],
                              o_out: torch.Tensor, lse_out: torch.Tensor, stream=None):
     check_merge_args(o_parts, lse_parts, o_out, lse_out)

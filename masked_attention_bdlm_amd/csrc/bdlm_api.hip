@@ -225,7 +225,7 @@ int bdlm_attn_fwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
 
 namespace {
 
-// The backward behind bdlm_attn_bwd.  `ws_of` is
+// The backward behind bdlm_attn_bwd and bdlm_attn_bwd_noalloc.  `ws_of` is
 // called once every argument has been validated, with the workspace size the
 // call needs; it returns the workspace (or NULL with *err set).
 template <typename WsOf>
@@ -345,6 +345,32 @@ int bwd_impl(const bdlm_attn_desc* desc, const void* qc, const void* kc, const v
   return BDLM_OK;
 }
 
+// ------------------------------------------------ scratch of the no-alloc call
+// The workspace of bdlm_attn_bwd_noalloc: one array per GPU, part of the
+// library's device image (no allocation call), held until the process ends.
+// Host code never uses the array's name as an address: the device address of
+// each GPU's copy comes from hipGetSymbolAddress with that GPU current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch copy (looked up once per device).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BDLM_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BDLM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BDLM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -357,6 +383,23 @@ int bdlm_attn_bwd(const bdlm_attn_desc* desc, const void* qc, const void* kc, co
   auto ws_of = [&](size_t need, int* err) -> void* {
     if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) *err = BDLM_ERR_WORKSPACE;
     return ws;
+  };
+  return bwd_impl(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox, dqc, dkc, dvc, dqx, dkx, dvx,
+                  ws_of, stream);
+}
+
+size_t bdlm_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int bdlm_attn_bwd_noalloc(const bdlm_attn_desc* desc, const void* qc, const void* kc, const void* vc,
+                          const void* qx, const void* kx, const void* vx, const void* oc, const void* ox,
+                          const float* lse_c, const float* lse_x, const void* doc, const void* dox,
+                          void* dqc, void* dkc, void* dvc, void* dqx, void* dkx, void* dvx,
+                          hipStream_t stream) {
+  auto ws_of = [&](size_t need, int* err) -> void* {
+    if (need > kScratchBytes) { *err = BDLM_ERR_UNSUPPORTED; return nullptr; }
+    void* p = nullptr;
+    *err = scratch_of_current_device(&p);
+    return p;
   };
   return bwd_impl(desc, qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox, dqc, dkc, dvc, dqx, dkx, dvx,
                   ws_of, stream);

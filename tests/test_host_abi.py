@@ -290,3 +290,19 @@ def test_staged_window_descriptor_and_walk():
         b, sb_ = M.schedule_walk(_ok_desc(kv_staged=0, **sd), fb)
         assert (a == b).all() and sa == sb_
 
+
+def test_noalloc_backward_refuses_oversize_before_any_device_call():
+    """The no-alloc backward's fixed workspace (64 MiB per GPU) bounds the
+    problem size; a larger one returns BDLM_ERR_UNSUPPORTED after argument
+    validation and before the device is touched (so this runs without a GPU)."""
+    lib = M.load()
+    assert lib.bdlm_attn_noalloc_scratch_bytes() == 64 << 20
+    p = ctypes.c_void_p(4096)
+    big = make_desc(1, 262144, 1024, 32, 8, 128, 1, 128 ** -0.5)
+    assert lib.bdlm_attn_workspace_bytes(ctypes.byref(big), 1) > 64 << 20
+    assert lib.bdlm_attn_bwd_noalloc(ctypes.byref(big), *([p] * 18), None) == 2
+    # the largest full-mode problem of the workloads (2L = 256K, 32 q heads) fits
+    fits = make_desc(1, 131072, 1024, 32, 8, 128, 1, 128 ** -0.5)
+    assert lib.bdlm_attn_workspace_bytes(ctypes.byref(fits), 1) <= 64 << 20
+    # invalid arguments are reported first, as by bdlm_attn_bwd
+    assert lib.bdlm_attn_bwd_noalloc(ctypes.byref(big), *([p] * 17), None, None) == 1
