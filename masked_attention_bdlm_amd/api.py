@@ -285,8 +285,9 @@ def merge_partials(o_parts: List[torch.Tensor], lse_parts: List[torch.Tensor],
 
 
 # ---------------------------------------------------------------- diagnostics
-def schedule_walk(desc, for_bwd: bool, want_cover: bool = True):
-    """Host walk of the kernels' work decomposition (batch 0, q-head 0).
+def schedule_walk(desc, for_bwd: int, want_cover: bool = True):
+    """Host walk of a kernel's work decomposition (batch 0, q-head 0): for_bwd
+    0 = forward, 1 = dK/dV kernel, 2 = dQ kernel.
 
     Returns (cover uint8 [rows, keys] or None, stats dict)."""
     import numpy as np
@@ -295,7 +296,9 @@ def schedule_walk(desc, for_bwd: bool, want_cover: bool = True):
     keys = desc.seqlen * 2 if desc.num_local_blocks == 0 else desc.seqlen + desc.num_local_blocks * desc.block
     cover = np.zeros((rows, keys), dtype=np.uint8) if want_cover else None
     stats = (ctypes.c_int64 * 5)()
-    st = lib.bdlm_attn_schedule_walk(ctypes.byref(desc), int(bool(for_bwd)),
+    if for_bwd not in (0, 1, 2):
+        raise ValueError("for_bwd: 0 forward, 1 dK/dV kernel, 2 dQ kernel")
+    st = lib.bdlm_attn_schedule_walk(ctypes.byref(desc), int(for_bwd),
                                      cover.ctypes.data_as(ctypes.c_void_p) if want_cover else None,
                                      cover.size if want_cover else 0, stats)
     check("bdlm_attn_schedule_walk", st)

@@ -480,7 +480,9 @@ int bdlm_attn_schedule_walk(const bdlm_attn_desc* desc, int for_bwd, uint8_t* co
         if (klo >= khi) continue;
         for (int k0 = klo; k0 < khi; k0 += 64) {
           ++visits;
-          const bool need_mask = !(k0 >= flo && k0 + 64 <= fhi);
+          // the forward and dQ kernels' own element-mask tests
+          const bool need_mask = for_bwd == 0 ? key_tile_partial(k0, 64, flo, fhi)
+                                              : qmajor_tile_masked(k0, 64, flo, fhi, r0, r1, kFwdTileM);
           masked += need_mask;
           for (int r = r0; r < r1; ++r) {
             int lo, hi;
@@ -493,6 +495,7 @@ int bdlm_attn_schedule_walk(const bdlm_attn_desc* desc, int for_bwd, uint8_t* co
       }
     }
   } else {
+    // the dK/dV kernel's iteration order and packed per-iteration decode
     const int ns0 = p.mode == 0 ? 0 : 1;
     int nkt[2], kbase[2], kend[2];
     if (p.mode == 1) {
@@ -514,24 +517,22 @@ int bdlm_attn_schedule_walk(const bdlm_attn_desc* desc, int for_bwd, uint8_t* co
       const int a = item < nkt[0] ? 0 : 1;
       const int j = a == 0 ? item : item - nkt[0];
       const int k0 = kbase[a] + j * kBwdTileN, k1 = std::min(k0 + kBwdTileN, kend[a]);
-      for (int s = (a == 0 ? ns0 : 1); s < 2; ++s) {
-        if (p.rows[s] == 0) continue;
-        int rlo, rhi;
-        query_span(p, s, a, k0, k1, rlo, rhi);
-        if (rlo >= rhi) continue;
-        for (int t = (rhi - 1) / M; t >= rlo / M; --t) {
-          const int q0 = t * M, q1 = std::min(q0 + M, p.rows[s]);
-          int klo, khi, flo, fhi;
-          tile_ranges(p, s, a, q0, q1, klo, khi, flo, fhi);
-          const bool need_mask = !(k0 >= flo && k0 + kBwdTileN <= fhi);
-          ++visits;
-          masked += need_mask;
-          for (int r = q0; r < q1; ++r) {
-            int lo, hi;
-            row_keys(p, s, r, a, lo, hi);
-            for (int k = k0; k < k1; ++k) {
-              if (need_mask ? (k >= lo && k < hi) : true) mark(s, r, a, k);
-            }
+      BwdOrder ord;
+      ord.init(p, a, ns0, k0, k1, M);
+      for (int it = 0; it < ord.total; ++it) {
+        const unsigned e = bwd_entry(p, ord, a, k0, kBwdTileN, M, it);
+        if (entry_head(e) != 0) continue;          // q-head 0 of kv head 0
+        const int s = entry_stream(e);
+        const int q0 = entry_tile(e) * M, q1 = std::min(q0 + M, p.rows[s]);
+        const bool need_mask = entry_masked(e);
+        ++visits;
+        masked += need_mask;
+        // unmasked: every row of the M-row tile and every key of the workgroup
+        for (int r = q0; r < (need_mask ? q1 : q0 + M); ++r) {
+          int lo = 0, hi = 0;
+          if (r < p.rows[s]) row_keys(p, s, r, a, lo, hi);
+          for (int k = k0; k < k1; ++k) {
+            if (need_mask ? (k >= lo && k < hi) : true) mark(s, r, a, k);
           }
         }
       }

@@ -117,6 +117,92 @@ __host__ __device__ inline void tile_ranges(const Problem& p, int s, int a, int 
   if (fhi < flo) fhi = flo;
 }
 
+// Whether key tile [k0, k0 + N) leaves the range [flo, fhi) that every row of
+// a query tile sees (then its elements are tested against each row's range).
+__host__ __device__ inline bool key_tile_partial(int k0, int N, int flo, int fhi) {
+  return !(k0 >= flo && k0 + N <= fhi);
+}
+// The same, or a short query tile (rows [r0, r1) with rows past the stream end).
+__host__ __device__ inline bool qmajor_tile_masked(int k0, int N, int flo, int fhi, int r0, int r1, int M) {
+  return key_tile_partial(k0, N, flo, fhi) || (r1 - r0 < M);
+}
+
+// Iteration order of a key-major backward workgroup (keys [k0, k1) of array
+// a): query tiles of M rows descending; at each tile position the (up to two)
+// query streams that see the keys, then the q heads of the GQA group, so the
+// workgroups of one kv head sweep the same query tiles together.
+struct BwdOrder {
+  int s0, s1, thi0, thi1, inter, tb, slow, nboth, n0, total;
+
+  __host__ __device__ inline void init(const Problem& p, int a, int ns0, int k0, int k1, int M) {
+    int tlo0 = 0, tlo1 = 0, nseg = 0;
+    s0 = s1 = thi0 = thi1 = 0;
+    for (int s = (a == 0 ? ns0 : 1); s < 2; ++s) {
+      if (p.rows[s] == 0) continue;
+      int rlo, rhi;
+      query_span(p, s, a, k0, k1, rlo, rhi);
+      if (rlo >= rhi) continue;
+      if (nseg == 0) { s0 = s; tlo0 = rlo / M; thi0 = (rhi - 1) / M; }
+      else { s1 = s; tlo1 = rlo / M; thi1 = (rhi - 1) / M; }
+      ++nseg;
+    }
+    const int G = p.group;
+    inter = (nseg == 2 && thi0 == thi1) ? 1 : 0;
+    tb = inter ? (tlo0 > tlo1 ? tlo0 : tlo1) : 0;
+    slow = tlo0 <= tlo1 ? s0 : s1;
+    nboth = inter ? (thi0 - tb + 1) * 2 * G : 0;
+    n0 = nseg > 0 ? (thi0 - tlo0 + 1) * G : 0;
+    total = inter ? nboth + (tb - (tlo0 < tlo1 ? tlo0 : tlo1)) * G
+                  : n0 + (nseg > 1 ? (thi1 - tlo1 + 1) * G : 0);
+  }
+
+  // Stream s, query tile t and head-in-group hg of iteration it.
+  __host__ __device__ inline void decode(const Problem& p, int it, int& s, int& t, int& hg) const {
+    if (inter) {
+      if (it < nboth) {
+        const int u = div_g(p, it);
+        t = thi0 - (u >> 1);
+        s = (u & 1) ? s1 : s0;
+        hg = mod_g(p, it);
+      } else {
+        const int r = it - nboth;
+        t = tb - 1 - div_g(p, r);
+        s = slow;
+        hg = mod_g(p, r);
+      }
+    } else if (it < n0) {
+      t = thi0 - div_g(p, it);
+      s = s0;
+      hg = mod_g(p, it);
+    } else {
+      const int r = it - n0;
+      t = thi1 - div_g(p, r);
+      s = s1;
+      hg = mod_g(p, r);
+    }
+  }
+};
+
+// Packed state of key-major iteration it: query tile | stream << 19 |
+// element-mask flag << 20 | head-in-group << 21.  The flag is set when the key
+// tile [k0, k0 + N) is not inside the range every row of the query tile sees,
+// or the query tile is short (rows past the stream end).
+__host__ __device__ inline unsigned bwd_entry(const Problem& p, const BwdOrder& o, int a, int k0, int N, int M,
+                                              int it) {
+  int s, t, hg;
+  o.decode(p, it, s, t, hg);
+  const int q0 = t * M;
+  const int q1 = q0 + M < p.rows[s] ? q0 + M : p.rows[s];
+  int klo, khi, flo, fhi;
+  tile_ranges(p, s, a, q0, q1, klo, khi, flo, fhi);
+  const unsigned m = qmajor_tile_masked(k0, N, flo, fhi, q0, q1, M) ? 1u : 0u;
+  return (unsigned)t | ((unsigned)s << 19) | (m << 20) | ((unsigned)hg << 21);
+}
+__host__ __device__ inline int entry_tile(unsigned e) { return (int)(e & 0x7FFFFu); }
+__host__ __device__ inline int entry_stream(unsigned e) { return (int)((e >> 19) & 1u); }
+__host__ __device__ inline bool entry_masked(unsigned e) { return (e >> 20) & 1u; }
+__host__ __device__ inline int entry_head(unsigned e) { return (int)(e >> 21); }
+
 // Key row of C-layout element i (0..15) held by lane half hh in a 32x32 MFMA
 // output tile: rows 8*(i/4) + 4*hh + (i%4).
 __host__ __device__ inline int c_row(int i, int hh) { return ((i >> 2) << 3) + (hh << 2) + (i & 3); }

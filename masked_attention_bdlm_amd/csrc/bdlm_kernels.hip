@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
     __syncthreads();   // tile `it` is in buffer it&1; buffer (it+1)&1 is free
     const T* k_lds = kv_lds[it & 1][0];
     const T* v_lds = kv_lds[it & 1][1];
-    const bool need_mask = !(k0 >= flo[a] && k0 + N <= fhi[a]);
+    const bool need_mask = key_tile_partial(k0, N, flo[a], fhi[a]);
     const int mylo = a ? lo[1] : lo[0], myhi = a ? hi[1] : hi[0];
 
     // S^T[key][query] for the N keys of the tile; K fragments are read in
@@ -402,62 +402,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs args) {
 }
 
 // ==================================================== backward: dK/dV kernel
-// Iteration order of a key-major backward workgroup: query tiles descending; at
-// each tile position the (up to two) query streams that see the key tile, then
-// the q heads of the GQA group.  Workgroups of one kv head therefore sweep the
-// same query tiles at the same time.  The order is a handful of uniform
-// integers: o[0..11] = s0, s1, tlo0, thi0, tlo1, thi1, inter, tb, slow,
-// nboth, n0, total.
-__device__ __forceinline__ void bwd_order(const Problem& p, int a, int ns0, int k0, int k1, int M, int* o) {
-  int s0 = 0, s1 = 0, tlo0 = 0, tlo1 = 0, thi0 = 0, thi1 = 0, nseg = 0;
-  for (int s = (a == 0 ? ns0 : 1); s < 2; ++s) {
-    if (p.rows[s] == 0) continue;
-    int rlo, rhi;
-    query_span(p, s, a, k0, k1, rlo, rhi);
-    if (rlo >= rhi) continue;
-    if (nseg == 0) { s0 = s; tlo0 = rlo / M; thi0 = (rhi - 1) / M; }
-    else { s1 = s; tlo1 = rlo / M; thi1 = (rhi - 1) / M; }
-    ++nseg;
-  }
-  const int G = p.group;
-  const int inter = (nseg == 2 && thi0 == thi1) ? 1 : 0;
-  const int tb = inter ? max(tlo0, tlo1) : 0;
-  const int nboth = inter ? (thi0 - tb + 1) * 2 * G : 0;
-  const int n0 = nseg > 0 ? (thi0 - tlo0 + 1) * G : 0;
-  o[0] = s0; o[1] = s1; o[2] = tlo0; o[3] = thi0; o[4] = tlo1; o[5] = thi1;
-  o[6] = inter; o[7] = tb; o[8] = tlo0 <= tlo1 ? s0 : s1; o[9] = nboth; o[10] = n0;
-  o[11] = inter ? nboth + (tb - min(tlo0, tlo1)) * G : n0 + (nseg > 1 ? (thi1 - tlo1 + 1) * G : 0);
-}
-
-#define BWD_DECODE(it, s, q0, h)                                   \
-  do {                                                             \
-    int t_, hg_;                                                   \
-    if (o_inter) {                                                 \
-      if ((it) < o_nboth) {                                        \
-        const int u_ = div_g(p, (it));                             \
-        t_ = o_thi0 - (u_ >> 1);                                   \
-        s = (u_ & 1) ? o_s1 : o_s0;                                \
-        hg_ = mod_g(p, (it));                                      \
-      } else {                                                     \
-        const int r_ = (it) - o_nboth;                             \
-        t_ = o_tb - 1 - div_g(p, r_);                              \
-        s = o_slow;                                                \
-        hg_ = mod_g(p, r_);                                        \
-      }                                                            \
-    } else if ((it) < o_n0) {                                      \
-      t_ = o_thi0 - div_g(p, (it));                                \
-      s = o_s0;                                                    \
-      hg_ = mod_g(p, (it));                                        \
-    } else {                                                       \
-      const int r_ = (it) - o_n0;                                  \
-      t_ = o_thi1 - div_g(p, r_);                                  \
-      s = o_s1;                                                    \
-      hg_ = mod_g(p, r_);                                          \
-    }                                                              \
-    q0 = t_ * M;                                                   \
-    h = g * G + hg_;                                               \
-  } while (0)
-
 // Key-major dK/dV: one workgroup per (batch, kv-head, key array, 128-key
 // tile); wave w owns 32 keys and keeps K_w, V_w (MFMA B operands) and its dK_w,
 // dV_w accumulators in registers while it sweeps the visible 64-row query
@@ -526,29 +470,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs args) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) { dkacc[dt] = f32x16{}; dvacc[dt] = f32x16{}; }
 
-  int o[12];
-  bwd_order(p, a, args.ns0, k0, k1, M, o);
-  const int o_s0 = o[0], o_s1 = o[1], o_thi0 = o[3], o_thi1 = o[5], o_inter = o[6], o_tb = o[7];
-  const int o_slow = o[8], o_nboth = o[9], o_n0 = o[10], total = o[11];
+  BwdOrder ord;
+  ord.init(p, a, args.ns0, k0, k1, M);
+  const int total = ord.total;
   const int G = p.group;
   const int64_t qrs = (int64_t)p.hq * D;
 
-  // Per-iteration state, decoded 64 iterations at a time (one per lane, as
-  // vector code) and packed: query tile | stream << 19 | mask << 20 |
-  // head-in-group << 21.  An iteration then costs two lane reads instead of
+  // Per-iteration state (bwd_entry), decoded 64 iterations at a time (one per
+  // lane, as vector code).  An iteration then costs two lane reads instead of
   // the branchy scalar decode, which all waves of the CU would otherwise run
   // on the shared scalar unit.
-#define DKDV_ENTRY(idx, out)                                                                     \
-  do {                                                                                           \
-    int s_e, q0_e, h_e;                                                                          \
-    BWD_DECODE(idx, s_e, q0_e, h_e);                                                             \
-    const int R_e = s_e ? rows1 : rows0;                                                         \
-    const int q1_e = min(q0_e + M, R_e);                                                         \
-    int klo_e, khi_e, flo_e, fhi_e;                                                              \
-    tile_ranges(p, s_e, a, q0_e, q1_e, klo_e, khi_e, flo_e, fhi_e);                              \
-    const unsigned m_e = (!(k0 >= flo_e && k0 + N <= fhi_e) || (q1_e - q0_e < M)) ? 1u : 0u;    \
-    out = (unsigned)(q0_e / M) | ((unsigned)s_e << 19) | (m_e << 20) | ((unsigned)(h_e - g * G) << 21); \
-  } while (0)
+#define DKDV_ENTRY(idx, out) out = bwd_entry(p, ord, a, k0, N, M, (idx))
   unsigned ent0 = 0, ent1 = 0;
   int ent_base = 0;
   if (total > 0) {
@@ -791,27 +723,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
   const int64_t krs = (int64_t)p.hkv * D;
   const int64_t qrs = (int64_t)p.hq * D;
 
-  int o[12];
-  bwd_order(p, a, args.ns0, k0, k1, M, o);
-  const int o_s0 = o[0], o_s1 = o[1], o_thi0 = o[3], o_thi1 = o[5], o_inter = o[6], o_tb = o[7];
-  const int o_slow = o[8], o_nboth = o[9], o_n0 = o[10], total = o[11];
+  BwdOrder ord;
+  ord.init(p, a, args.ns0, k0, k1, M);
+  const int total = ord.total;
   const int G = p.group;
 
-  // Iteration (tile) i's state, decoded 64 at a time, one per lane:
-  // query tile | stream << 19 | mask << 20 | head-in-group << 21.
+  // Iteration (tile) i's state (bwd_entry), decoded 64 at a time, one per lane.
   unsigned ent = 0;
   int ent_base = 0;
-#define WS_ENTRY(idx, out)                                                                       \
-  do {                                                                                           \
-    int s_e, q0_e, h_e;                                                                          \
-    BWD_DECODE(idx, s_e, q0_e, h_e);                                                             \
-    const int R_e = s_e ? rows1 : rows0;                                                         \
-    const int q1_e = min(q0_e + M, R_e);                                                         \
-    int klo_e, khi_e, flo_e, fhi_e;                                                              \
-    tile_ranges(p, s_e, a, q0_e, q1_e, klo_e, khi_e, flo_e, fhi_e);                              \
-    const unsigned m_e = (!(k0 >= flo_e && k0 + N <= fhi_e) || (q1_e - q0_e < M)) ? 1u : 0u;    \
-    out = (unsigned)(q0_e / M) | ((unsigned)s_e << 19) | (m_e << 20) | ((unsigned)(h_e - g * G) << 21); \
-  } while (0)
+#define WS_ENTRY(idx, out) out = bwd_entry(p, ord, a, k0, N, M, (idx))
   // entry of tile x; x never decreases between calls of one wave
 #define WS_GET(x, out)                                                                           \
   do {                                                                                           \
@@ -1139,7 +1059,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
     __syncthreads();   // tile `it` is in buffer it&1; buffer (it+1)&1 is free
     const T* k_lds = kv_lds[it & 1][0];
     const T* v_lds = kv_lds[it & 1][1];
-    const bool need_mask = !(k0 >= flo[a] && k0 + N <= fhi[a]) || (r1 - r0 < M);
+    const bool need_mask = qmajor_tile_masked(k0, N, flo[a], fhi[a], r0, r1, M);
     const int mylo = a ? lo[1] : lo[0], myhi = a ? hi[1] : hi[0];
 
     // per 32-key sub-tile: S^T = K Q^T and dP^T = V dO^T, then
