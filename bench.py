@@ -337,6 +337,9 @@ def bench_share(args, w, dev, stream):
         "pct_of_peak": round(100.0 * useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "useful_flop_per_step": useful,
         "kernels_ms_per_step": {k: round(v["total_ms"] / args.steps, 4) for k, v in kernels.items()},
+        "fwd_ms": round(sum(kernels.get(n, {}).get("total_ms", 0.0) for n in ("bdlm_fwd", "bdlm_merge")) / args.steps, 4),
+        "bwd_ms": round(sum(kernels.get(n, {}).get("total_ms", 0.0)
+                            for n in ("bdlm_bwd_pre", "bdlm_dkdv", "bdlm_dq")) / args.steps, 4),
         "kernel_launches_per_step": {k: v["launches"] // args.steps for k, v in kernels.items()},
         "roofline": roof,
         "kernel_roofline": per_kernel,
@@ -671,6 +674,10 @@ def main():
         "strict_12_tflops": round(strict / (ms * 1e-3) / 1e12, 3),
         "useful_flop_per_step": useful,
         "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in kernels.items()},
+        # forward and backward separately (per step, from the kernels' HIP events)
+        "fwd_ms": round(kernels.get("bdlm_fwd", {}).get("total_ms", 0.0) / args.steps, 4),
+        "bwd_ms": round(sum(kernels.get(n, {}).get("total_ms", 0.0)
+                            for n in ("bdlm_bwd_pre", "bdlm_dkdv", "bdlm_dq")) / args.steps, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
