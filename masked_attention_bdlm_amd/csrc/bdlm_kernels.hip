@@ -234,6 +234,21 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
       dma_rows<T, N, D>(kv_lds[(it + 1) & 1][1], vb[a2], rs, k02, khi[a2], w, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // The V^T fragments of the first two d-tiles do not depend on P: read
+    // them now, so that their latency hides behind the softmax.
+    Frag va[3][N / KC];
+    auto rd_va = [&](int dt) {
+#pragma unroll
+      for (int cc = 0; cc < N / KC; ++cc) {
+        if constexpr (OFFS)
+          va[dt % 3][cc] = ld_fragT(reinterpret_cast<const char*>(v_lds), offT, OFFS ? dt : 0,
+                                    ((cc / CPS) * 32 + 16 * (cc % CPS)) * D * 2);
+        else
+          va[dt % 3][cc] = ld_frag_kcrow_s<T, D>(v_lds, (cc / CPS) * 32, cc % CPS, lane, dt * 32);
+      }
+    };
+    rd_va(0);
+    if (D / 32 > 1) rd_va(1);
 
     // Edge tiles only (one uniform branch): keys outside the row's range.
     if (need_mask) {
@@ -286,29 +301,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
 #pragma unroll
     for (int cc = 0; cc < N / KC; ++cc) pb[cc] = pack_frag<T>(&pv[cc / CPS][(cc % CPS) * KPL]);
     {
-      Frag va[2][N / KC];
-#pragma unroll
-      for (int cc = 0; cc < N / KC; ++cc) {
-        if constexpr (OFFS)
-          va[0][cc] = ld_fragT(reinterpret_cast<const char*>(v_lds), offT, 0, ((cc / CPS) * 32 + 16 * (cc % CPS)) * D * 2);
-        else
-          va[0][cc] = ld_frag_kcrow_s<T, D>(v_lds, (cc / CPS) * 32, cc % CPS, lane, 0);
-      }
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        if (dt + 1 < D / 32) {
-#pragma unroll
-          for (int cc = 0; cc < N / KC; ++cc) {
-            if constexpr (OFFS)
-              va[(dt + 1) & 1][cc] = ld_fragT(reinterpret_cast<const char*>(v_lds), offT, OFFS ? dt + 1 : 0,
-                                              ((cc / CPS) * 32 + 16 * (cc % CPS)) * D * 2);
-            else
-              va[(dt + 1) & 1][cc] = ld_frag_kcrow_s<T, D>(v_lds, (cc / CPS) * 32, cc % CPS, lane, (dt + 1) * 32);
-          }
-        }
+        if (dt + 2 < D / 32) rd_va(dt + 2);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cc = 0; cc < N / KC; ++cc) oacc[dt] = E::mma(va[dt & 1][cc], pb[cc], oacc[dt]);
+        for (int cc = 0; cc < N / KC; ++cc) oacc[dt] = E::mma(va[dt % 3][cc], pb[cc], oacc[dt]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -768,12 +766,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
         WS_GET(it, e);
         // S and dP for rows qs*32 .. +31 (rows = queries, column = this lane's key)
         f32x16 sacc = f32x16{}, pacc = f32x16{};
-        // Q / dO fragments read two k-chunks ahead of their MFMAs (3-slot ring)
-        bf16x8 qa[3], da[3];
+        // Q / dO fragments read three k-chunks ahead of their MFMAs (4-slot ring)
+        bf16x8 qa[4], da[4];
         auto rd = [&](int c) {
           const char* ap = tb + offA[c] + qs * 32 * D * 2;
-          qa[c % 3] = *reinterpret_cast<const bf16x8*>(ap);
-          da[c % 3] = *reinterpret_cast<const bf16x8*>(ap + L::TILE);
+          qa[c % 4] = *reinterpret_cast<const bf16x8*>(ap);
+          da[c % 4] = *reinterpret_cast<const bf16x8*>(ap + L::TILE);
         };
         // The rows' LSE and D values (C-layout rows of this lane) are read in
         // the middle of the MFMA chain, so that they have landed at its end.
@@ -789,13 +787,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
         };
         rd(0);
         if (L::DCH > 1) rd(1);
+        if (L::DCH > 2) rd(2);
 #pragma unroll
         for (int c = 0; c < L::DCH; ++c) {
-          if (c + 2 < L::DCH) rd(c + 2);
+          if (c + 3 < L::DCH) rd(c + 3);
           if (c == L::DCH / 2 - 1) rd_rows();
           __builtin_amdgcn_sched_barrier(0);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c % 3], kf[c], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[c % 3], vf[c], pacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c % 4], kf[c], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[c % 4], vf[c], pacc, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
         // P and dS in the C layout (k of the consumer's MFMAs = queries)
@@ -904,7 +903,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
         }
         // dV_w += P^T dO ; dK_w += dS^T Q.  The transposed dO / Q fragments of
         // column block dt + 1 are read while the MFMAs of block dt run.
-        bf16x8 ob[2][2], qb[2][2];
+        bf16x8 ob[3][2], qb[3][2];
         auto read_t = [&](int dt, bf16x8 (&o)[2], bf16x8 (&q)[2]) {
 #pragma unroll
           for (int ci = 0; ci < 2; ++ci) {
@@ -917,20 +916,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
                           __builtin_bit_cast(bf16x4, ds_read_tr16(b1)));
           }
         };
-        // (for block 0 after its first MFMA pair, behind the P/dS reads, so
-        // that at most 12 LDS reads are outstanding: the wait counter holds 15)
         read_t(0, ob[0], qb[0]);
 #pragma unroll
         for (int dt = 0; dt < L::DT; ++dt) {
-          if (dt >= 1 && dt + 1 < L::DT) read_t(dt + 1, ob[(dt + 1) & 1], qb[(dt + 1) & 1]);
+          if (dt >= 1 && dt + 2 < L::DT) read_t(dt + 2, ob[(dt + 2) % 3], qb[(dt + 2) % 3]);
           __builtin_amdgcn_sched_barrier(0);
-          dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfr[0], ob[dt & 1][0], dvacc[dt], 0, 0, 0);
-          dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sfr[0], qb[dt & 1][0], dkacc[dt], 0, 0, 0);
+          dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfr[0], ob[dt % 3][0], dvacc[dt], 0, 0, 0);
+          dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sfr[0], qb[dt % 3][0], dkacc[dt], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           if (dt == 0 && L::DT > 1) read_t(1, ob[1], qb[1]);
+          if (dt == 0 && L::DT > 2) read_t(2, ob[2], qb[2]);
           __builtin_amdgcn_sched_barrier(0);
-          dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfr[1], ob[dt & 1][1], dvacc[dt], 0, 0, 0);
-          dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sfr[1], qb[dt & 1][1], dkacc[dt], 0, 0, 0);
+          dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfr[1], ob[dt % 3][1], dvacc[dt], 0, 0, 0);
+          dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sfr[1], qb[dt % 3][1], dkacc[dt], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1106,12 +1104,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
       }
       // The first d-tile's K^T fragments do not depend on dS: read them now,
       // so that their latency hides behind the DMA issue and the exponentials.
-      Frag kt[2][CPS];
+      Frag kt[3][CPS];
+      auto rd_kt = [&](int dt) {
 #pragma unroll
-      for (int ci = 0; ci < CPS; ++ci) {
-        if constexpr (OFFS) kt[0][ci] = ld_fragT(reinterpret_cast<const char*>(k_lds), offT, 0, (sub * 32 + 16 * ci) * D * 2);
-        else kt[0][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, 0);
-      }
+        for (int ci = 0; ci < CPS; ++ci) {
+          if constexpr (OFFS)
+            kt[dt % 3][ci] = ld_fragT(reinterpret_cast<const char*>(k_lds), offT, OFFS ? dt : 0, (sub * 32 + 16 * ci) * D * 2);
+          else
+            kt[dt % 3][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, dt * 32);
+        }
+      };
+      rd_kt(0);
+      if (D / 32 > 1) rd_kt(1);
       // Next tile's DMA, issued behind the first sub-tile's S^T / dP^T MFMAs
       // (a wave stalls while the memory pipeline accepts DMA instructions).
       if (sub == 0 && it + 1 < total) {
@@ -1144,19 +1148,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
       {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          if (dt + 1 < D / 32) {
-#pragma unroll
-            for (int ci = 0; ci < CPS; ++ci) {
-              if constexpr (OFFS)
-                kt[(dt + 1) & 1][ci] = ld_fragT(reinterpret_cast<const char*>(k_lds), offT, OFFS ? dt + 1 : 0,
-                                                (sub * 32 + 16 * ci) * D * 2);
-              else
-                kt[(dt + 1) & 1][ci] = ld_frag_kcrow_s<T, D>(k_lds, sub * 32, ci, lane, (dt + 1) * 32);
-            }
-          }
+          if (dt + 2 < D / 32) rd_kt(dt + 2);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int ci = 0; ci < CPS; ++ci) acc[dt] = E::mma(kt[dt & 1][ci], dsf[ci], acc[dt]);
+          for (int ci = 0; ci < CPS; ++ci) acc[dt] = E::mma(kt[dt % 3][ci], dsf[ci], acc[dt]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
