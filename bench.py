@@ -42,7 +42,7 @@ PEAK_HBM_GBS = 8000.0
 # the counters are taken again.
 MEASURED_TRAFFIC = {
     "kernel": "bdlm_dkdv",
-    "sources_sha256": "055e217b88b80a66f20bebf8f9ed0d327f28f9ddd8adae4682c11df25ffa222f",
+    "sources_sha256": "0694fba203434932e6abb01f08862d443f66d931e0fed9405e2733ad219e7ab3",
     "fetch_kib": 1.1945241e7, "fetch_scale": 2.0,
     "write_kib": 2.62144e5, "write_scale": 1.0,
 }

@@ -295,8 +295,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArg
       }
     }
 
-    // O^T[d][query] += V^T[d][key] P^T[key][query]; the V^T fragments of one
-    // d-tile are read while the previous d-tile's MFMAs run
+    // O^T[d][query] += V^T[d][key] P^T[key][query]; the V^T fragments of each
+    // d-tile are read two d-tiles ahead of its MFMAs (3-slot ring)
     Frag pb[N / KC];
 #pragma unroll
     for (int cc = 0; cc < N / KC; ++cc) pb[cc] = pack_frag<T>(&pv[cc / CPS][(cc % CPS) * KPL]);
@@ -902,7 +902,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_ws_kernel(BwdArgs args) {
           sfr[ci] = *reinterpret_cast<const bf16x8*>(pd + 2048 + ci * 1024);
         }
         // dV_w += P^T dO ; dK_w += dS^T Q.  The transposed dO / Q fragments of
-        // column block dt + 1 are read while the MFMAs of block dt run.
+        // each column block are read two blocks ahead of its MFMAs (3-slot ring).
         bf16x8 ob[3][2], qb[3][2];
         auto read_t = [&](int dt, bf16x8 (&o)[2], bf16x8 (&q)[2]) {
 #pragma unroll
@@ -1102,8 +1102,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void dq_kernel(DqArgs 
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // The first d-tile's K^T fragments do not depend on dS: read them now,
-      // so that their latency hides behind the DMA issue and the exponentials.
+      // The K^T fragments of the first two d-tiles do not depend on dS: read
+      // them now, so that their latency hides behind the DMA issue and the
+      // exponentials; the others are read two d-tiles ahead (3-slot ring).
       Frag kt[3][CPS];
       auto rd_kt = [&](int dt) {
 #pragma unroll
