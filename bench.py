@@ -526,6 +526,47 @@ def bench_memory(args, dev, stream):
     print(json.dumps(out), flush=True)
 
 
+def bench_mfma_ceiling(dev, stream, iters: int = 1600000):
+    """Sustained bf16 MFMA rate for four operand / instruction mixes
+    (bdlm_calib_mfma, one launch of every SIMD's matrix core kept busy for
+    about 0.2 s each): how far below the published 2516.6 TFLOP/s the chip's
+    power limit holds the clock, and so the rate a fully busy matrix core
+    reaches, with constant operands, random ones, and random ones beside the
+    attention kernels' LDS operand traffic (1 KB per MFMA) or VALU work."""
+    import torch
+    from masked_attention_bdlm_amd.api import bdlm_calib_mfma
+    wg = torch.cuda.get_device_properties(dev).multi_processor_count
+    cycles = torch.zeros(wg * 16, dtype=torch.int64, device=dev)
+    sink = torch.zeros(wg * 512, dtype=torch.float32, device=dev)
+    names = ("constant_operands", "random_operands", "random_operands_lds_1KB_per_mfma",
+             "random_operands_4_fma_per_mfma")
+    modes = {}
+    for mode, name in enumerate(names):
+        bdlm_calib_mfma(mode, wg, iters // 10 // 2 * 2, cycles, sink, stream)   # warm the clock
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bdlm_calib_mfma(mode, wg, iters, cycles, sink, stream)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        c = cycles.view(-1, 2).double().cpu()
+        clock = float(c[:, 0].sum() / c[:, 1].sum()) * 0.1          # GHz (ticks at 100 MHz)
+        flop = wg * 8.0 * iters * 4 * 32768.0
+        tf = flop / (ms * 1e-3) / 1e12
+        modes[name] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                       "clock_GHz": round(clock, 3), "ms": round(ms, 2)}
+        log(f"mfma ceiling {name}: {tf:.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:.1f} % of peak) "
+            f"at {clock:.2f} GHz, {ms:.1f} ms")
+    line = {
+        "metric": "sustained bf16 MFMA TFLOP/s, every SIMD's matrix core busy (v_mfma_f32_32x32x16_bf16, "
+                  "8 waves per CU), random operands",
+        "value": modes["random_operands"]["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+        "higher_is_better": True, "peak": PEAK_BF16_TFLOPS, "workgroups": wg, "iters_per_wave": iters,
+        "flop_per_launch": wg * 8.0 * iters * 4 * 32768.0, "modes": modes,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -538,6 +579,8 @@ def main():
                     help="with a rank-share workload: time all ranks under the contiguous and zigzag layouts")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter calibration)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure the bf16 MFMA rate the chip sustains (calibration of the peak)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -566,6 +609,9 @@ def main():
         return
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.mfma_ceiling:
+        bench_mfma_ceiling(dev, stream)
+        return
     if args.workload == "csbp_memory":
         bench_memory(args, dev, stream)
         return

@@ -276,6 +276,30 @@ typedef struct {
 int bdlm_attn_profile_begin(int32_t max_launches);
 int bdlm_attn_profile_end(bdlm_kernel_time* out, int32_t max_entries, int32_t* num_entries);
 
+/*
+ * Calibration (diagnostics; not part of the attention path): the bf16 MFMA
+ * rate the chip sustains under a given operand and instruction mix.  The
+ * published dense peak assumes the 2.4 GHz peak clock; under load the chip
+ * holds its power limit by lowering the clock, and how far depends on the
+ * operand bits that toggle.  Launches `workgroups` workgroups of 8 waves (two
+ * per SIMD, one workgroup per CU) on `stream`; every wave runs `iters` (even,
+ * >= 2) steps of 4 v_mfma_f32_32x32x16_bf16 (32768 flop each) on four
+ * independent accumulators, plus per mode:
+ *   0  constant operands;
+ *   1  random operands (bf16 uniform in [-0.5, 0.5), 8 register sets in turn);
+ *   2  mode 1 plus one 16-byte LDS read per lane per MFMA (1 KB per wave and
+ *      MFMA, the attention kernels' LDS operand traffic), read 4 MFMAs ahead;
+ *   3  mode 1 plus 4 FMAs per MFMA.
+ * cycles: device int64 [workgroups * 8 * 2], per wave {shader-clock cycles,
+ * 100 MHz real-time ticks} over its MFMA loop (clock = cycles / ticks * 0.1 GHz).
+ * sink: device float [workgroups * 512], written so no work is removed.  The
+ * caller times the launch (events on `stream`): rate = workgroups * 8 * iters
+ * * 4 * 32768 flop / time.  Returns BDLM_ERR_INVALID_ARG before any device work
+ * for a bad mode, size or null pointer, BDLM_ERR_HIP if the launch fails.
+ */
+int bdlm_calib_mfma(int32_t mode, int32_t workgroups, int32_t iters, int64_t* cycles, float* sink,
+                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

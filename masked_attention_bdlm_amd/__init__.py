@@ -11,9 +11,11 @@ from .api import (  # noqa: F401
     attention_bwd,
     attention_fwd,
     bdlm_attn_bwd,
+    bdlm_attn_bwd_noalloc,
     bdlm_attn_fwd,
     bdlm_attn_merge_partials,
     bdlm_attn_workspace_bytes,
+    bdlm_calib_mfma,
     desc_for,
     merge_partials,
     schedule_walk,

@@ -23,7 +23,7 @@ EXPORTED = (
     "bdlm_attn_workspace_bytes", "bdlm_attn_check_desc", "bdlm_attn_fwd", "bdlm_attn_bwd",
     "bdlm_attn_merge_partials", "bdlm_attn_schedule_walk", "bdlm_status_str",
     "bdlm_attn_version", "bdlm_attn_profile_begin", "bdlm_attn_profile_end",
-    "bdlm_attn_bwd_noalloc", "bdlm_attn_noalloc_scratch_bytes",
+    "bdlm_attn_bwd_noalloc", "bdlm_attn_noalloc_scratch_bytes", "bdlm_calib_mfma",
 )
 
 
@@ -88,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.bdlm_attn_profile_begin.restype = ctypes.c_int
     lib.bdlm_attn_profile_end.argtypes = [ctypes.POINTER(BdlmKernelTime), i32, ctypes.POINTER(i32)]
     lib.bdlm_attn_profile_end.restype = ctypes.c_int
+    lib.bdlm_calib_mfma.argtypes = [i32, i32, i32, vp, vp, vp]
+    lib.bdlm_calib_mfma.restype = ctypes.c_int
     _lib = lib
     return lib
 

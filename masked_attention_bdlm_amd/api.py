@@ -306,6 +306,18 @@ def schedule_walk(desc, for_bwd: int, want_cover: bool = True):
     return cover, dict(zip(names, [int(x) for x in stats]))
 
 
+def bdlm_calib_mfma(mode: int, workgroups: int, iters: int, cycles: torch.Tensor, sink: torch.Tensor,
+                    stream=None):
+    """Calibration launch of the sustained bf16 MFMA probe (modes 0-3, see
+    include/bdlm_attn.h); cycles: int64 [workgroups * 16], sink: float32
+    [workgroups * 512], both on the GPU."""
+    _expect(cycles, "cycles", (workgroups * 16,), torch.int64)
+    _expect(sink, "sink", (workgroups * 512,), torch.float32, cycles.device)
+    st = load().bdlm_calib_mfma(int(mode), int(workgroups), int(iters), _ptr(cycles), _ptr(sink),
+                                _stream(stream, cycles))
+    check("bdlm_calib_mfma", st)
+
+
 class KernelTimer:
     """Context manager around bdlm_attn_profile_begin/end: per-kernel HIP-event
     totals of every launch the library makes inside the block."""

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdlm_attn.so")
-SOURCES = ["bdlm_api.hip", "bdlm_kernels.hip"]
+SOURCES = ["bdlm_api.hip", "bdlm_kernels.hip", "bdlm_calib.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

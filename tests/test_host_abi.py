@@ -306,3 +306,17 @@ def test_noalloc_backward_refuses_oversize_before_any_device_call():
     assert lib.bdlm_attn_workspace_bytes(ctypes.byref(fits), 1) <= 64 << 20
     # invalid arguments are reported first, as by bdlm_attn_bwd
     assert lib.bdlm_attn_bwd_noalloc(ctypes.byref(big), *([p] * 17), None, None) == 1
+
+
+def test_calibration_probe_rejects_bad_arguments_before_any_device_call():
+    """bdlm_calib_mfma (the sustained-MFMA calibration launch) validates its
+    mode, sizes and pointers before touching the device (runs without a GPU)."""
+    lib = M.load()
+    p = ctypes.c_void_p(4096)
+    assert lib.bdlm_calib_mfma(4, 256, 1000, p, p, None) == 1      # no such mode
+    assert lib.bdlm_calib_mfma(-1, 256, 1000, p, p, None) == 1
+    assert lib.bdlm_calib_mfma(1, 0, 1000, p, p, None) == 1        # no workgroups
+    assert lib.bdlm_calib_mfma(1, 256, 999, p, p, None) == 1       # odd step count
+    assert lib.bdlm_calib_mfma(1, 256, 0, p, p, None) == 1
+    assert lib.bdlm_calib_mfma(1, 256, 1000, None, p, None) == 1   # null outputs
+    assert lib.bdlm_calib_mfma(1, 256, 1000, p, None, None) == 1
