@@ -46,6 +46,12 @@ SMALL = [
     _case("bf16_b48", 144, 48, 2, 2, 128, "bf16"),
     _case("bf16_one_block", 128, 128, 2, 1, 128, "bf16", sharp=True),
     _case("bf16_many_tiles", 1024, 64, 8, 2, 128, "bf16", sharp=True),
+    # GQA group of 3 (the head decode divides), last 64-row tile of 16 rows
+    _case("bf16_g3_short_tail", 208, 16, 6, 2, 128, "bf16", batch=2, sharp=True),
+    _case("f32_g3", 96, 32, 3, 1, 64, "f32", sharp=True),
+    # problems shorter than one 64-row query tile
+    _case("bf16_L48_g3", 48, 16, 3, 1, 64, "bf16"),
+    _case("bf16_L32_one_block", 32, 32, 2, 2, 128, "bf16", sharp=True),
 ]
 
 

@@ -136,6 +136,9 @@ FULL_CASES = [
     (128, 128, 1, 1, 64, 1),    # B = L: one block
     (144, 48, 2, 2, 128, 0),    # B not a power of two
     (96, 16, 3, 1, 64, 1),
+    (208, 16, 6, 2, 128, 1),    # GQA group 3, last 64-row tile of 16 rows
+    (48, 16, 3, 1, 64, 1),      # shorter than one 64-row tile
+    (32, 32, 2, 2, 128, 1),     # one block shorter than one tile
 ]
 
 
