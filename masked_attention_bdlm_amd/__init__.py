@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     bdlm_attn_bwd_noalloc,
     bdlm_attn_fwd,
     bdlm_attn_merge_partials,
+    bdlm_attention,
     bdlm_attn_workspace_bytes,
     bdlm_calib_mfma,
     desc_for,

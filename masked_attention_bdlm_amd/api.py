@@ -237,6 +237,34 @@ def attention_bwd(qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox, block:
     return dqc, dkc, dvc, dqx, dkx, dvx
 
 
+class _BdlmAttention(torch.autograd.Function):
+    """Full-mode BDLM attention as an autograd function.  Forward and backward
+    are the library's bdlm_attn_fwd and bdlm_attn_bwd; the saved tensors are
+    the inputs, O and the LSE rows (the backward recomputes P from them)."""
+
+    @staticmethod
+    def forward(ctx, qc, kc, vc, qx, kx, vx, block, scale):
+        oc, ox, lse_c, lse_x = attention_fwd(qc, kc, vc, qx, kx, vx, block, scale)
+        ctx.save_for_backward(qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x)
+        ctx.block, ctx.scale = block, scale
+        return oc, ox
+
+    @staticmethod
+    def backward(ctx, doc, dox):
+        qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x = ctx.saved_tensors
+        doc = torch.zeros_like(oc) if doc is None else doc.contiguous()
+        dox = torch.zeros_like(ox) if dox is None else dox.contiguous()
+        grads = attention_bwd(qc, kc, vc, qx, kx, vx, oc, ox, lse_c, lse_x, doc, dox, ctx.block, ctx.scale)
+        return (*grads, None, None)
+
+
+def bdlm_attention(qc, kc, vc, qx, kx, vx, block: int, scale: Optional[float] = None):
+    """Differentiable full-mode BDLM attention over [x0 ; xt]: returns (oc, ox).
+    Inputs are [batch, L, heads, d] device tensors as for attention_fwd; the
+    gradients of qc, kc, vc, qx, kx, vx come from bdlm_attn_bwd."""
+    return _BdlmAttention.apply(qc, kc, vc, qx, kx, vx, block, scale)
+
+
 def share_fwd(qx, kx, vx, kc, vc, block_ids, block: int, kv_begin: int, kv_end: int,
               own_block: int, scale: Optional[float] = None, out=None, stream=None, clean_queries: int = 0,
               accumulate: int = 0, seqlen: Optional[int] = None, kv_staged: int = 0):
